@@ -1,0 +1,52 @@
+/*
+ * gqo.h — CPU oracle for GGUF block-quantized matmul.  TEST INFRASTRUCTURE ONLY.
+ *
+ * This header belongs to the oracle alone.  Only tests/, the smoke check and the
+ * CPU-baseline leg of bench.py load the library built from gqo.c.  The GPU library
+ * shares no code, header, table or helper with it.
+ *
+ * All pointers are host pointers owned by the caller.  Every function returns 0 on
+ * success and a negative value on a bad argument (unknown type, shape not a whole
+ * number of blocks, null pointer).
+ *
+ * Type codes (this project's own numbering; the pages give none):
+ *   0 F32, 1 F16, 2 Q4_0, 3 Q5_0, 4 Q8_0, 5 Q4_K, 6 Q6_K
+ */
+#ifndef GQO_H
+#define GQO_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { GQO_F32 = 0, GQO_F16 = 1, GQO_Q4_0 = 2, GQO_Q5_0 = 3, GQO_Q8_0 = 4,
+       GQO_Q4_K = 5, GQO_Q6_K = 6 };
+
+/* Weights per block and bytes per block of a quantized type. */
+int gqo_block_info(int type, int64_t *block_elems, int64_t *block_bytes);
+
+/* fp16 helpers, written from the IEEE binary16 definition. */
+double   gqo_half_to_double(uint16_t h);
+uint16_t gqo_half_up(double v);     /* smallest finite fp16 >= v, v >= 0; 0x7C00 if none */
+uint16_t gqo_half_rne(float f);     /* round-to-nearest-even fp32 -> fp16 */
+
+/* Quantize row-major fp32 w[rows][cols] into a blob of rows*(cols/QK) blocks. */
+int gqo_quantize(int type, const float *w, int64_t rows, int64_t cols, uint8_t *blob);
+
+/* Dequantize a blob.  _f32 follows the stated fp32 operation order; _f64 is exact. */
+int gqo_dequant_f32(int type, const uint8_t *blob, int64_t rows, int64_t cols, float *out);
+int gqo_dequant_f64(int type, const uint8_t *blob, int64_t rows, int64_t cols, double *out);
+
+/*
+ * y[t][r] = sum_c W^[r][c] * x[t][c] in fp64 (dequant-then-dot, sequential over c).
+ * yabs[t][r] = sum_c |W^[r][c] * x[t][c]| (the tolerance scale); yabs may be NULL.
+ * threads <= 0 means one thread.  Rows are split over OpenMP threads only.
+ */
+int gqo_matmul_f64(int type, const uint8_t *blob, int64_t rows, int64_t cols,
+                   const double *x, int64_t n_tok, double *y, double *yabs, int threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,238 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Each ``pin_*`` function raises AssertionError when the given oracle instance
+disagrees with what the pages or mathematics fix.  ``tests/test_oracle.py`` runs
+them on the real oracle (all must pass) and on builds with a deliberate mistake
+compiled in (at least one must fail for each).
+
+What each pin rests on:
+  * golden blocks: hand-chosen fields packed by the byte layouts of the pages
+    (or the stated readings), with weights from the pages' dequant formulas;
+  * byte counts and bits per weight printed on the pages;
+  * exact rational arithmetic (fractions.Fraction) for the fp64 dot;
+  * textbook reductions: Q8_0 with d = 1 is an integer matrix product (NumPy
+    int64), Q4_K with constant codes per sub-block reduces to per-sub-block sums;
+  * invariants: power-of-two scaling is exact, row permutation permutes y,
+    n tokens in one call equal n calls;
+  * the quantizer's round-trip error bound derived from its definition.
+"""
+from __future__ import annotations
+
+import glob
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+QTYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k"]
+
+
+def golden_fixtures():
+    out = []
+    for p in sorted(glob.glob(os.path.join(GOLDEN, "*.json"))):
+        with open(p) as fh:
+            out.append((os.path.basename(p), json.load(fh)))
+    return out
+
+
+def pin_golden(o):
+    """Hand-built blocks decode to the pages' formula on their fields."""
+    for name, fx in golden_fixtures():
+        raw = np.frombuffer(bytes.fromhex(fx["hex"]), dtype=np.uint8)
+        qk, bb = o.block_info(fx["type"])
+        assert raw.size == bb, name
+        w64 = o.dequant_f64(raw, fx["type"], 1, qk)[0]
+        w32 = o.dequant_f32(raw, fx["type"], 1, qk)[0]
+        exp = np.array(fx["expected"], dtype=np.float64)
+        exp32 = np.array(fx["expected_f32"], dtype=np.float32)
+        assert np.array_equal(w64, exp), (name, np.nonzero(w64 != exp)[0][:5])
+        assert np.array_equal(w32.view(np.uint32), exp32.view(np.uint32)), name
+
+
+def pin_sizes(o):
+    """Bytes per block and bits per weight as the pages print them."""
+    # Q4_0: 18 B per 32 weights, 4.5 bpw (Hitchhiker's Guide §11.1 figure).
+    assert o.block_info("q4_0") == (32, 18)
+    # Q4_K: 2+2+12+128 = 144 B per 256 weights, 4.5 bpw (§11.2; 12 — llama.cpp).
+    assert o.block_info("q4_k") == (256, 2 + 2 + 12 + 128)
+    for t in ("q4_0", "q4_k"):
+        qk, bb = o.block_info(t)
+        assert bb * 8 / qk == 4.5
+    # Q6_K: the "Other k-quants" table prints 6.6 bits per weight.
+    qk, bb = o.block_info("q6_k")
+    assert qk == 256 and round(bb * 8 / qk, 1) == 6.6
+    # Q8_0 (Q4_0 structure, 8-bit codes) and Q5_0 (4+1 bit codes).
+    assert o.block_info("q8_0") == (32, 2 + 32)
+    assert o.block_info("q5_0") == (32, 2 + 4 + 16)
+
+
+def _exact_dot(w64, x):
+    out = []
+    for r in range(w64.shape[0]):
+        s = Fraction(0)
+        sa = Fraction(0)
+        for c in range(w64.shape[1]):
+            p = Fraction(float(w64[r, c])) * Fraction(float(x[c]))
+            s += p
+            sa += abs(p)
+        out.append((s, sa))
+    return out
+
+
+def pin_fraction_dot(o):
+    """fp64 dot within the sequential-summation bound of the exact rational dot."""
+    for k, t in enumerate(QTYPES):
+        qk, _ = o.block_info(t)
+        rows, cols = 3, 2 * qk
+        w = synth.weights(rows, cols, seed=100 + k, outlier_frac=0.05)
+        blob = o.quantize(w, t)
+        w64 = o.dequant_f64(blob, t, rows, cols)
+        x = synth.dyadic((2, cols), seed=200 + k)
+        y, yabs = o.matmul_f64(blob, t, rows, cols, x)
+        for tok in range(2):
+            for r, (s, sa) in enumerate(_exact_dot(w64, x[tok])):
+                bound = cols * 2.0 ** -53 * float(sa)
+                assert abs(Fraction(y[tok, r]) - s) <= Fraction(bound), (t, tok, r)
+                assert abs(Fraction(yabs[tok, r]) - sa) <= Fraction(bound), (t, tok, r)
+
+
+def _q8_blob(codes: np.ndarray) -> np.ndarray:
+    """Q8_0 blob with d = 1.0 (fp16 0x3C00) and the given int8 codes [rows, cols]."""
+    rows, cols = codes.shape
+    blocks = codes.reshape(rows, cols // 32, 32).astype(np.int8).view(np.uint8)
+    head = np.zeros((rows, cols // 32, 2), dtype=np.uint8)
+    head[..., 0], head[..., 1] = 0x00, 0x3C
+    return np.concatenate([head, blocks], axis=2).reshape(-1)
+
+
+def pin_q8_integer(o):
+    """Q8_0 with d = 1 and integer x is an exact integer matrix product."""
+    rng = np.random.default_rng(7)
+    rows, cols, n = 5, 96, 3
+    codes = rng.integers(-128, 128, size=(rows, cols))
+    xi = rng.integers(-1000, 1000, size=(n, cols))
+    y, _ = o.matmul_f64(_q8_blob(codes), "q8_0", rows, cols, xi.astype(np.float64))
+    assert np.array_equal(y, (xi @ codes.T).astype(np.float64))
+
+
+def _q4k_const_blob(d16, dmin16, sc, mn, code):
+    """One Q4_K block whose 256 codes all equal ``code`` (layout-order free)."""
+    v = 0
+    for i in range(8):
+        v |= sc[i] << (12 * i)
+        v |= mn[i] << (12 * i + 6)
+    head = bytes([d16 & 0xFF, d16 >> 8, dmin16 & 0xFF, dmin16 >> 8]) + v.to_bytes(12, "little")
+    return np.frombuffer(head + bytes([code | (code << 4)]) * 128, dtype=np.uint8)
+
+
+def pin_q4k_structured(o):
+    """Constant codes: y = sum_i (d*sc_i*c - dmin*m_i) * (sum of x over sub-block i)."""
+    sc = [3, 60, 17, 1, 44, 9, 33, 25]
+    mn = [5, 0, 63, 12, 7, 30, 2, 48]
+    d, dmin = 0.0078125, 0.001953125          # fp16 0x2000, 0x1800
+    x = synth.dyadic((1, 256), seed=11)
+    for code in (0, 5, 15):
+        blob = _q4k_const_blob(0x2000, 0x1800, sc, mn, code)
+        y, _ = o.matmul_f64(blob, "q4_k", 1, 256, x)
+        want = sum((d * sc[i] * code - dmin * mn[i]) * x[0, 32 * i:32 * i + 32].sum()
+                   for i in range(8))
+        assert abs(y[0, 0] - want) <= 1e-12 * max(1.0, abs(want)), (code, y[0, 0], want)
+
+
+def pin_pow2_and_perm(o):
+    """Doubling d (and dmin) doubles y exactly; permuting rows permutes y."""
+    offs = {"q4_0": [0], "q5_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0]}
+    for k, t in enumerate(QTYPES):
+        qk, bb = o.block_info(t)
+        rows, cols = 6, 2 * qk
+        w = synth.weights(rows, cols, seed=300 + k)
+        blob = o.quantize(w, t)
+        x = synth.activations(2, cols, seed=400 + k).astype(np.float64)
+        y, _ = o.matmul_f64(blob, t, rows, cols, x)
+        b2 = blob.copy().reshape(-1, bb)
+        for off in offs[t]:
+            h = b2[:, off].astype(np.uint16) | (b2[:, off + 1].astype(np.uint16) << 8)
+            mag = h & 0x7FFF
+            assert np.all((mag >> 10) < 30)               # room for one more exponent step
+            # normal: exponent + 1; subnormal (and zero): the encoding doubles
+            h = np.where(mag >= 0x0400, h + 0x0400, (h & 0x8000) | (mag << 1)).astype(np.uint16)
+            b2[:, off] = (h & 0xFF).astype(np.uint8)
+            b2[:, off + 1] = (h >> 8).astype(np.uint8)
+        y2, _ = o.matmul_f64(b2.reshape(-1), t, rows, cols, x)
+        assert np.array_equal(y2, 2.0 * y), t
+        rb = cols // qk * bb
+        perm = np.random.default_rng(k).permutation(rows)
+        bp = blob.reshape(rows, rb)[perm].reshape(-1)
+        yp, _ = o.matmul_f64(bp, t, rows, cols, x)
+        assert np.array_equal(yp, y[:, perm]), t
+        # n tokens in one call equal one call per token
+        for tok in range(2):
+            y1, _ = o.matmul_f64(blob, t, rows, cols, x[tok:tok + 1])
+            assert np.array_equal(y1[0], y[tok]), t
+
+
+def pin_f32_is_one_rounding(o):
+    """The fp32 dequant rounds at most once: it equals fp32(fp64 dequant)."""
+    for k, t in enumerate(QTYPES):
+        qk, _ = o.block_info(t)
+        rows, cols = 8, 4 * qk
+        w = synth.weights(rows, cols, seed=500 + k, outlier_frac=0.01)
+        blob = o.quantize(w, t)
+        w32 = o.dequant_f32(blob, t, rows, cols)
+        w64 = o.dequant_f64(blob, t, rows, cols)
+        assert np.array_equal(w32, w64.astype(np.float32)), t
+
+
+def _roundtrip_bound(w: np.ndarray, t: str) -> np.ndarray:
+    """Per-weight bound on |w - dequant(quantize(w))| from the quantizer's
+    definition (covering fp16 scales rounded up by at most 2^-10 relative,
+    codes rounded to nearest)."""
+    up = 1.0 + 2.0 ** -9
+    w = w.astype(np.float64)
+    if t in ("q4_0", "q5_0", "q8_0"):
+        L = {"q4_0": 7, "q5_0": 15, "q8_0": 127}[t]
+        a = np.abs(w.reshape(-1, 32)).max(axis=1, keepdims=True)
+        d = a / L * up + 2.0 ** -24
+        return np.broadcast_to(d / 2, (a.shape[0], 32)).reshape(w.shape)
+    if t == "q6_k":
+        ts = np.abs(w.reshape(-1, 16, 16)).max(axis=2, keepdims=True) / 31.0
+        d = ts.max(axis=1, keepdims=True) / 127.0 * up + 2.0 ** -24             # [blocks,1,1]
+        step = ts + d
+        return np.broadcast_to(step / 2, (ts.shape[0], 16, 16)).reshape(w.shape)
+    # q4_k
+    sb = w.reshape(-1, 8, 32)
+    lo = np.minimum(sb.min(axis=2), 0.0)
+    hi = sb.max(axis=2)
+    M = -lo
+    dmin = M.max(axis=1, keepdims=True) / 63.0 * up + 2.0 ** -24
+    sp = (hi + M + dmin) / 15.0
+    d = sp.max(axis=1, keepdims=True) / 63.0 * up + 2.0 ** -24
+    step = sp + d
+    return np.broadcast_to((step / 2)[..., None], sb.shape).reshape(w.shape)
+
+
+def pin_roundtrip(o):
+    """Quantize -> dequantize stays within half a quantization step."""
+    for k, t in enumerate(QTYPES):
+        qk, _ = o.block_info(t)
+        rows, cols = 16, 4 * qk
+        for frac in (0.0, 0.01):
+            w = synth.weights(rows, cols, seed=600 + k, outlier_frac=frac)
+            blob = o.quantize(w, t)
+            err = np.abs(o.dequant_f64(blob, t, rows, cols) - w.astype(np.float64))
+            bound = _roundtrip_bound(w, t) * (1 + 1e-9) + 1e-12
+            assert np.all(err <= bound), (t, frac, float((err / bound).max()))
+        # special blocks: all zero, all equal, all positive
+        for w in (np.zeros((1, qk), np.float32), np.full((1, qk), 0.03, np.float32),
+                  np.abs(synth.weights(1, qk, seed=7))):
+            blob = o.quantize(w, t)
+            err = np.abs(o.dequant_f64(blob, t, 1, qk) - w.astype(np.float64))
+            assert np.all(err <= _roundtrip_bound(w, t) * (1 + 1e-9) + 1e-12), t
+
+
+ALL_PINS = [pin_golden, pin_sizes, pin_fraction_dot, pin_q8_integer, pin_q4k_structured,
+            pin_pow2_and_perm, pin_f32_is_one_rounding, pin_roundtrip]
