@@ -1,0 +1,140 @@
+// gq_api.cpp — the C ABI declared in include/gq.h: argument validation on the
+// host, then dispatch to the kernel families.  Every check runs before the
+// first HIP call, so the validation is testable on a machine with no GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gq.h"
+#include "gq_launch.h"
+
+namespace {
+
+constexpr int64_t kDim = (int64_t)1 << 31;       // rows, cols, n_tok < 2^31
+constexpr int64_t kBytes = (int64_t)1 << 47;     // any one buffer < 2^47 bytes
+constexpr int64_t kMaxColsGemv = 16384;          // x staged in 64 KB of LDS
+constexpr int64_t kMaxTokens = (int64_t)1 << 22;  // matrix-core grid.y = n_tok / 64 < 65536
+constexpr int64_t kMaxElems = (int64_t)1 << 40;   // dequant / quantize grid.x < 2^31
+
+bool quant_type(int t) { return t >= GQ_Q4_0 && t <= GQ_Q6_K; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na > 0 && nb > 0 && x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+
+int check_matrix(int type, int64_t rows, int64_t cols, int64_t* rb) {
+  if (!quant_type(type)) return GQ_EINVAL_TYPE;
+  if (rows < 1 || cols < 1) return GQ_EINVAL_SHAPE;
+  if (rows >= kDim || cols >= kDim) return GQ_EOVERFLOW;
+  int64_t r = gq_row_bytes(type, cols);
+  if (r < 0) return (int)r;
+  if (rows > kBytes / r) return GQ_EOVERFLOW;
+  *rb = r;
+  return GQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gq_type_info(int type, int64_t* block_elems, int64_t* block_bytes) {
+  int64_t qk, bb;
+  switch (type) {
+    case GQ_F32:  qk = 1;   bb = 4;   break;
+    case GQ_F16:  qk = 1;   bb = 2;   break;
+    case GQ_Q4_0: qk = 32;  bb = 18;  break;
+    case GQ_Q5_0: qk = 32;  bb = 22;  break;
+    case GQ_Q8_0: qk = 32;  bb = 34;  break;
+    case GQ_Q4_K: qk = 256; bb = 144; break;
+    case GQ_Q6_K: qk = 256; bb = 210; break;
+    default: return GQ_EINVAL_TYPE;
+  }
+  if (block_elems) *block_elems = qk;
+  if (block_bytes) *block_bytes = bb;
+  return GQ_OK;
+}
+
+int64_t gq_row_bytes(int type, int64_t cols) {
+  int64_t qk, bb;
+  int rc = gq_type_info(type, &qk, &bb);
+  if (rc) return rc;
+  if (cols < 1 || cols % qk) return GQ_EINVAL_SHAPE;
+  if (cols >= kDim) return GQ_EOVERFLOW;
+  return cols / qk * bb;
+}
+
+const char* gq_strerror(int code) {
+  switch (code) {
+    case GQ_OK: return "success";
+    case GQ_EINVAL_TYPE: return "unknown or unsupported type";
+    case GQ_EINVAL_SHAPE: return "invalid shape (rows/cols < 1, cols not a whole number of blocks, or n_tok < 0)";
+    case GQ_EINVAL_PTR: return "null pointer or overlapping input/output ranges";
+    case GQ_EALIGN: return "pointer not 16-byte aligned";
+    case GQ_EOVERFLOW: return "size beyond the supported range";
+    case GQ_EHIP: return "HIP launch failed";
+  }
+  return "unknown error code";
+}
+
+int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols,
+                 const void* x, int x_type, float* y, int64_t n_tok, void* stream) {
+  int64_t rb = 0;
+  int rc = check_matrix(ggml_type, rows, cols, &rb);
+  if (rc) return rc;
+  if (x_type != GQ_F32 && x_type != GQ_F16) return GQ_EINVAL_TYPE;
+  if (n_tok < 0) return GQ_EINVAL_SHAPE;
+  if (n_tok >= kDim) return GQ_EOVERFLOW;
+  if (n_tok == 0) return GQ_OK;
+  if (n_tok == 1 && cols > kMaxColsGemv) return GQ_EOVERFLOW;
+  if (n_tok > kMaxTokens) return GQ_EOVERFLOW;
+  if (n_tok > kBytes / cols || n_tok > kBytes / rows) return GQ_EOVERFLOW;
+  if (!weight_blob || !x || !y) return GQ_EINVAL_PTR;
+  if (!aligned16(weight_blob) || !aligned16(x) || !aligned16(y)) return GQ_EALIGN;
+  const int64_t xbytes = n_tok * cols * (x_type == GQ_F16 ? 2 : 4);
+  const int64_t ybytes = n_tok * rows * 4;
+  const int64_t wbytes = rows * rb;
+  if (overlap(x, xbytes, y, ybytes) || overlap(weight_blob, wbytes, y, ybytes))
+    return GQ_EINVAL_PTR;
+  hipStream_t st = (hipStream_t)stream;
+  const bool xf16 = (x_type == GQ_F16);
+  if (n_tok == 1) return hip_status(gq::launch_gemv(ggml_type, weight_blob, rows, cols, x, xf16, y, st));
+  return hip_status(gq::launch_mfma(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
+}
+
+int gq_matmul(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols, const void* x,
+              float* y, int64_t n_tok, void* stream) {
+  return gq_matmul_ex(weight_blob, ggml_type, rows, cols, x, GQ_F32, y, n_tok, stream);
+}
+
+int gq_dequant(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols, void* out,
+               int out_type, void* stream) {
+  int64_t rb = 0;
+  int rc = check_matrix(ggml_type, rows, cols, &rb);
+  if (rc) return rc;
+  if (out_type != GQ_F32 && out_type != GQ_F16) return GQ_EINVAL_TYPE;
+  if (rows > kMaxElems / cols) return GQ_EOVERFLOW;
+  if (!weight_blob || !out) return GQ_EINVAL_PTR;
+  if (!aligned16(weight_blob) || !aligned16(out)) return GQ_EALIGN;
+  const int64_t obytes = rows * cols * (out_type == GQ_F16 ? 2 : 4);
+  if (overlap(weight_blob, rows * rb, out, obytes)) return GQ_EINVAL_PTR;
+  return hip_status(gq::launch_dequant(ggml_type, weight_blob, rows, cols, out,
+                                       out_type == GQ_F16, (hipStream_t)stream));
+}
+
+int gq_quantize(const float* w, int ggml_type, int64_t rows, int64_t cols, void* weight_blob,
+                void* stream) {
+  int64_t rb = 0;
+  int rc = check_matrix(ggml_type, rows, cols, &rb);
+  if (rc) return rc;
+  if (rows > kMaxElems / cols) return GQ_EOVERFLOW;
+  if (!w || !weight_blob) return GQ_EINVAL_PTR;
+  if (!aligned16(w) || !aligned16(weight_blob)) return GQ_EALIGN;
+  if (overlap(w, rows * cols * 4, weight_blob, rows * rb)) return GQ_EINVAL_PTR;
+  return hip_status(gq::launch_quantize(ggml_type, w, rows, cols, weight_blob, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// gq_device.h — device-side helpers shared by libgq's kernels (gfx950 only).
+//
+// Block layouts are the ones declared in include/gq.h.  Everything here is
+// register-level bit manipulation on raw block bytes; no host code.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/gq.h"
+
+namespace gq {
+
+// Unaligned vector types: the blob's blocks are 18, 22, 34 or 210 bytes, so
+// block fields are generally not naturally aligned.  gfx950 global loads
+// accept unaligned addresses; these typedefs tell the compiler so.
+typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(1)));
+typedef uint32_t u32x2u __attribute__((ext_vector_type(2), aligned(1)));
+typedef uint32_t u32u __attribute__((aligned(1)));
+typedef uint16_t u16u __attribute__((aligned(1)));
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16u(const uint8_t* p) {
+  u32x4u v = *reinterpret_cast<const u32x4u*>(p);
+  return u32x4{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ u32x4 ld16a(const uint8_t* p) {   // 16-B aligned
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ u32x2 ld8u(const uint8_t* p) {
+  u32x2u v = *reinterpret_cast<const u32x2u*>(p);
+  return u32x2{v.x, v.y};
+}
+__device__ __forceinline__ uint32_t ld4u(const uint8_t* p) {
+  return *reinterpret_cast<const u32u*>(p);
+}
+__device__ __forceinline__ uint32_t ld2u(const uint8_t* p) {
+  return *reinterpret_cast<const u16u*>(p);
+}
+
+// fp16 bit pattern (low 16 bits of h) -> fp32, exact (subnormals included).
+__device__ __forceinline__ float h2f(uint32_t h) {
+  _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));
+  return (float)v;
+}
+
+// Byte k of w as an exact fp32 (compiles to v_cvt_f32_ubyte{k}).
+__device__ __forceinline__ float ub0(uint32_t w) { return (float)(w & 0xFFu); }
+__device__ __forceinline__ float ub1(uint32_t w) { return (float)((w >> 8) & 0xFFu); }
+__device__ __forceinline__ float ub2(uint32_t w) { return (float)((w >> 16) & 0xFFu); }
+__device__ __forceinline__ float ub3(uint32_t w) { return (float)(w >> 24); }
+
+// Byte k of w as a signed (two's complement) exact fp32 (v_cvt_f32_i32 with
+// a sign-extending byte select).
+__device__ __forceinline__ float sb0(uint32_t w) { return (float)(int)(int8_t)w; }
+__device__ __forceinline__ float sb1(uint32_t w) { return (float)(int)(int8_t)(w >> 8); }
+__device__ __forceinline__ float sb2(uint32_t w) { return (float)(int)(int8_t)(w >> 16); }
+__device__ __forceinline__ float sb3(uint32_t w) { return (float)((int)w >> 24); }
+
+// Four unsigned codes q (one per byte, q + 128 - off < 256) to the signed
+// bytes q - off: add 128 - off to every byte (no carries), flip the sign bit.
+template <int OFF>
+__device__ __forceinline__ uint32_t centre(uint32_t q4) {
+  return (q4 + (uint32_t)(128 - OFF) * 0x01010101u) ^ 0x80808080u;
+}
+
+// Block geometry.
+template <int T> struct Geo;
+template <> struct Geo<GQ_Q4_0> { static constexpr int QK = 32,  BB = 18;  };
+template <> struct Geo<GQ_Q5_0> { static constexpr int QK = 32,  BB = 22;  };
+template <> struct Geo<GQ_Q8_0> { static constexpr int QK = 32,  BB = 34;  };
+template <> struct Geo<GQ_Q4_K> { static constexpr int QK = 256, BB = 144; };
+template <> struct Geo<GQ_Q6_K> { static constexpr int QK = 256, BB = 210; };
+
+// A "segment" is 32 consecutive weights of a row: one block of the 32-weight
+// types, one sub-block of Q4_K, one 32-weight group of Q6_K.  Segment s of a
+// row lives in block s / (QK/32), part s % (QK/32).
+template <int T> struct SegAddr {
+  static constexpr int PER_BLOCK = Geo<T>::QK / 32;
+  __device__ static const uint8_t* block(const uint8_t* row, int s) {
+    return row + (size_t)(s / PER_BLOCK) * Geo<T>::BB;
+  }
+};
+
+// Q4_K: 12-bit (scale, min) pair of sub-block i from header dwords w0..w2
+// (bytes 4..15 of the block).  Field k sits at bits 6k..6k+5 of the 96-bit
+// little-endian stream, so sub-block i's pair is bits 12i..12i+11.
+__device__ __forceinline__ uint32_t q4k_pair(uint32_t w0, uint32_t w1, uint32_t w2, int i) {
+  uint64_t lo = (uint64_t)w0 | ((uint64_t)w1 << 32);
+  uint64_t hi = (uint64_t)w1 | ((uint64_t)w2 << 32);
+  int sh = 12 * i;
+  uint32_t v = (i <= 4) ? (uint32_t)(lo >> sh) : (uint32_t)(hi >> (sh - 32));
+  return v & 0xFFFu;
+}
+
+// Q6_K: the 2-bit high parts of one quarter of a 32-weight group, moved to
+// bits 4..5 of each byte.  hq is the qh dword holding bytes k = 4*(quarter&1)
+// .. +3 of the group's 8 qh bytes; u selects bits 2u..2u+1.
+__device__ __forceinline__ uint32_t q6k_hi(uint32_t hq, int u) {
+  // ((hq >> 2u) & 0x03030303) << 4
+  return (u <= 2 ? (hq << (4 - 2 * u)) : (hq >> (2 * u - 4))) & 0x30303030u;
+}
+
+// Spread 4 bits (b0..b3 of v) to bit 4 of bytes 0..3.
+__device__ __forceinline__ uint32_t spread4_bit4(uint32_t v) {
+  v &= 0xFu;
+  return ((v & 1u) << 4) | ((v & 2u) << 11) | ((v & 4u) << 18) | ((v & 8u) << 25);
+}
+
+// Wave64 sum with cross-lane swaps (result valid in every lane).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+}  // namespace gq

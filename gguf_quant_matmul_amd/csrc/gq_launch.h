@@ -1,0 +1,20 @@
+// gq_launch.h — host-side launchers implemented by the kernel files.
+// Arguments are already validated by gq_api.cpp when these are called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gq {
+
+hipError_t launch_dequant(int type, const void* blob, int64_t rows, int64_t cols, void* out,
+                          bool f16_out, hipStream_t st);
+hipError_t launch_quantize(int type, const float* w, int64_t rows, int64_t cols, void* blob,
+                           hipStream_t st);
+// One token (n_tok == 1): the bandwidth-bound GEMV family.
+hipError_t launch_gemv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
+                       bool x_f16, float* y, hipStream_t st);
+// n_tok >= 2: weights decoded once, reused for every token on the matrix cores.
+hipError_t launch_mfma(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
+                       bool x_f16, float* y, int64_t n_tok, hipStream_t st);
+
+}  // namespace gq

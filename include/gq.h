@@ -1,0 +1,148 @@
+/*
+ * gq.h — C ABI of libgq: matrix-vector and small-batch matrix multiplication
+ * over GGUF block-quantized weights on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The pages describe GGUF weights stored as blocks, each
+ * with its own fp16 scale ("Hitchhiker's Guide — Lab 01", §11.1, w ~= d*q),
+ * Q4_K super-blocks of 256 weights in 8 sub-blocks of 32 with 6-bit scales
+ * and mins under an fp16 super-scale and super-min (§11.2, dequant formula
+ * w = (d*sc)*q - dmin*m; "12 — llama.cpp / GGUF", section "Q4_K_M — bit layout
+ * in exquisite detail"), and the Q4_K_M recipe mixing Q4_K, Q5_0, Q6_K and
+ * Q8_0 blocks that are dequantized inside the dot product ("Local LLM
+ * inference", section "The mmap backend").  This library computes
+ *
+ *     y[t][r] = sum_c  W^[r][c] * x[t][c]      for t < n_tok, r < rows
+ *
+ * where W^ is the dequantized weight matrix.  Decode is memory-bound: each
+ * weight is read once per call ("The bandwidth cap", 12 — llama.cpp / GGUF).
+ *
+ * Conventions shared by every entry point:
+ *  - W is row-major: row r is the byte range [r*RB, (r+1)*RB) of the blob,
+ *    RB = gq_row_bytes(type, cols); blocks are contiguous within a row.
+ *    rows = output features, cols = input features (as in nn.Linear).
+ *  - x is [n_tok][cols], y is [n_tok][rows], both row-major, contiguous.
+ *  - Pointers marked "device" are HIP device (or managed) pointers; the
+ *    library never allocates, frees, or keeps caller memory.
+ *  - stream is a hipStream_t passed as void*; NULL is the null stream.  All
+ *    work is enqueued asynchronously; the library never synchronizes, so
+ *    device faults surface at the caller's next synchronization.
+ *  - All argument checks run on the host before any HIP call; on a failed
+ *    check nothing is enqueued.  Return value 0 is success, else a GQ_E* code.
+ *  - NaN or Inf in a block's scales propagates into y; it is not an error.
+ *  - The library is stateless and reentrant; calls may run concurrently on
+ *    different streams.
+ */
+#ifndef GQ_H
+#define GQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Block types.  The numbering is this library's own. */
+enum {
+    GQ_F32  = 0,   /* activations / outputs only */
+    GQ_F16  = 1,   /* activations / outputs only */
+    GQ_Q4_0 = 2,   /* 32 weights, 18 B:  fp16 d, 16 B codes; w = d*(q-8) */
+    GQ_Q5_0 = 3,   /* 32 weights, 22 B:  fp16 d, u32 fifth bits, 16 B codes; w = d*(q-16) */
+    GQ_Q8_0 = 4,   /* 32 weights, 34 B:  fp16 d, 32 int8 codes; w = d*q */
+    GQ_Q4_K = 5,   /* 256 weights, 144 B: fp16 d, fp16 dmin, 12 B 6-bit sc/m, 128 B codes */
+    GQ_Q6_K = 6    /* 256 weights, 210 B: fp16 d, 16 int8 scales, 128 B low, 64 B high bits */
+};
+
+/* Error codes. */
+enum {
+    GQ_OK            = 0,
+    GQ_EINVAL_TYPE   = -1,  /* unknown or unsupported type / x_type / out_type */
+    GQ_EINVAL_SHAPE  = -2,  /* rows < 1, cols < 1, cols % block size, n_tok < 0 */
+    GQ_EINVAL_PTR    = -3,  /* null pointer, or input and output ranges overlap */
+    GQ_EALIGN        = -4,  /* a pointer is not 16-byte aligned */
+    GQ_EOVERFLOW     = -5,  /* sizes beyond the supported range (see below) */
+    GQ_EHIP          = -6   /* a HIP launch failed (the HIP error is consumed) */
+};
+
+/*
+ * Byte layouts (all fields little-endian; readings where the pages are
+ * silent are marked R):
+ *  Q4_0: d @0; qs[16] @2; element j<16 = qs[j] & 15, j>=16 = qs[j-16] >> 4
+ *        ("How LLM Inference Engines Work", "Loading GGUF Models").
+ *  Q8_0: d @0; int8 q[32] @2 (R: two's complement).
+ *  Q5_0: d @0; u32 qh @2, bit j = bit 4 of code j; qs[16] @6 as Q4_0 (R).
+ *  Q4_K: d @0; dmin @2; scales[12] @4 = 16 six-bit fields, field k at bits
+ *        6k..6k+5 of the 96-bit little-endian stream (R), sub-block i uses
+ *        field 2i as scale and 2i+1 as min; qs[128] @16, sub-block i owns
+ *        bytes 16i..16i+15 in Q4_0 nibble order (R).
+ *        w = (d*sc_i)*q - dmin*m_i.
+ *  Q6_K: d @0; int8 scales[16] @2 (one per 16 weights); ql[128] @18, group g
+ *        of 32 owns bytes 16g..16g+15 in Q4_0 nibble order; qh[64] @146, byte
+ *        8g+k holds bits 4..5 of elements 32g+k+8u at bits 2u..2u+1 (R).
+ *        w = d*(sc*(q-32)).
+ *
+ * Limits: rows, cols and n_tok below 2^31; rows*RB, n_tok*cols and
+ * n_tok*rows below 2^47; cols <= 16384 at n_tok = 1 (x is staged in 64 KB of
+ * LDS); n_tok <= 2^22; rows*cols <= 2^40 for gq_dequant and gq_quantize.
+ * Beyond a limit the call returns GQ_EOVERFLOW.
+ */
+
+/* Weights per block and bytes per block of `type` (host only, no HIP call).
+ * Either output pointer may be NULL. */
+int gq_type_info(int type, int64_t *block_elems, int64_t *block_bytes);
+
+/* Bytes per row for `cols` weights of `type`; a negative GQ_E* code on a bad
+ * type or a cols that is not a whole number of blocks (host only). */
+int64_t gq_row_bytes(int type, int64_t cols);
+
+/* Static, human-readable text for an error code. */
+const char *gq_strerror(int code);
+
+/*
+ * y = W^ x with fp32 activations.  Equivalent to gq_matmul_ex(..., GQ_F32, ...).
+ *   weight_blob  device, rows*RB bytes, 16-B aligned, read only
+ *   x            device, fp32 [n_tok][cols], 16-B aligned, read only
+ *   y            device, fp32 [n_tok][rows], 16-B aligned, overwritten
+ * n_tok = 0 is a successful no-op.  x and y must not overlap each other or
+ * the blob.  Accumulation is fp32 throughout (the pages warn that fp16
+ * accumulation overflows: "How LLM Inference Engines Work", "Quantization").
+ */
+int gq_matmul(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
+              const void *x, float *y, int64_t n_tok, void *stream);
+
+/*
+ * As gq_matmul, with x_type GQ_F32 or GQ_F16 giving the activation format.
+ * For n_tok >= 2 the weights are decoded once per call and reused for every
+ * token ("Local LLM inference", "The mmap backend": decode each projection
+ * weight once per input batch) on the matrix cores; fp32 activations are then
+ * split exactly into two fp16 halves so no activation precision is lost.
+ */
+int gq_matmul_ex(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
+                 const void *x, int x_type, float *y, int64_t n_tok, void *stream);
+
+/*
+ * Dequantize the whole blob into out[rows][cols] (device, 16-B aligned).
+ *   out_type GQ_F32: bit-exact with the stated fp32 operation order: Q4_K
+ *     forms a = d*sc and b = dmin*m in fp32 (exact) and rounds once in
+ *     a*q - b; Q6_K forms the integer sc*(q-32) and multiplies by d (exact);
+ *     the 32-weight types compute d*(q - offset) (exact).
+ *   out_type GQ_F16: round-to-nearest-even of that fp32 value.
+ */
+int gq_dequant(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
+               void *out, int out_type, void *stream);
+
+/*
+ * Quantize fp32 w[rows][cols] (device) into a blob (device, rows*RB bytes),
+ * all arithmetic in fp64: symmetric absmax blocks for Q4_0 / Q5_0 / Q8_0 and
+ * for Q6_K's 16-weight sub-blocks, min/scale sub-blocks for Q4_K ("two-level
+ * scaling" and "asymmetric quantization", Hitchhiker's Guide §11.2); stored
+ * fp16 scales are rounded up so every weight is covered, codes are rounded
+ * half away from zero.  Weights whose block scale would exceed the largest
+ * finite fp16 saturate.  Used to make blobs from fp32 weights on the device.
+ */
+int gq_quantize(const float *w, int ggml_type, int64_t rows, int64_t cols,
+                void *weight_blob, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GQ_H */

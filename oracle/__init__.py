@@ -61,7 +61,7 @@ def _ptr(a: np.ndarray):
 class Oracle:
     def __init__(self, plant: int = 0):
         path = _lib_path(plant)
-        if not os.path.exists(path):
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_SRC):
             build(force=True, plant=plant)
         lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int

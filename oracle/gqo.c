@@ -338,9 +338,11 @@ static int clampi(double v, int lo, int hi) {
     return (int)v;
 }
 
-/* fp16 scale covering target: 63*d >= m-style checks use this with L. */
+/* Smallest fp16 scale d with levels*d >= maxval (checked in fp64), saturating
+ * at the largest finite fp16 when no finite scale covers maxval. */
 static uint16_t cover_scale(double maxval, double levels) {
     uint16_t h = gqo_half_up(maxval / levels);
+    if (h > 0x7BFF) h = 0x7BFF;      /* no finite cover: saturate at 65504 */
     /* make sure levels * d really covers maxval in fp64; bump one ulp if not */
     while (h < 0x7BFF && gqo_half_to_double(h) * levels < maxval) h++;
     return h;

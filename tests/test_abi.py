@@ -1,0 +1,77 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+
+import pytest
+
+import gguf_quant_matmul_amd as gq
+import oracle
+
+
+def test_exports_every_declared_symbol():
+    names = gq.header_symbols()
+    assert {"gq_matmul", "gq_matmul_ex", "gq_dequant", "gq_quantize", "gq_type_info",
+            "gq_row_bytes", "gq_strerror"} <= set(names)
+    L = gq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_type_info_matches_oracle_and_pages():
+    for t in gq.QUANT_TYPES:
+        assert gq.type_info(t) == oracle.block_info(t)
+    assert gq.type_info("q4_k") == (256, 144)      # Hitchhiker's Guide §11.2
+    assert gq.row_bytes("q6_k", 11008) == 9030
+    assert gq.row_bytes("q4_k", 4096) == 2304
+    with pytest.raises(gq.GQError):
+        gq.row_bytes("q4_k", 100)
+
+
+def test_strerror_covers_codes():
+    fallback = gq.strerror(-99)
+    assert fallback == "unknown error code"
+    msgs = [gq.strerror(c) for c in range(0, -7, -1)]
+    assert all(m and m != fallback for m in msgs) and len(set(msgs)) == 7
+
+
+A = 0x10000          # fake, 16-B aligned addresses: every call below must fail
+B = 0x20000          # a check before touching them
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A, 99, 16, 256, B, 0x30000, 1, None), -1),            # bad type
+    ((A, gq.F32, 16, 256, B, 0x30000, 1, None), -1),        # F32 is not a weight type
+    ((A, gq.Q4_K, 16, 100, B, 0x30000, 1, None), -2),       # cols % 256
+    ((A, gq.Q4_K, 0, 256, B, 0x30000, 1, None), -2),        # rows < 1
+    ((A, gq.Q4_K, 16, 256, B, 0x30000, -1, None), -2),      # n_tok < 0
+    ((None, gq.Q4_K, 16, 256, B, 0x30000, 1, None), -3),    # null blob
+    ((A, gq.Q4_K, 16, 256, None, 0x30000, 1, None), -3),    # null x
+    ((A + 4, gq.Q4_K, 16, 256, B, 0x30000, 1, None), -4),   # misaligned blob
+    ((A, gq.Q4_K, 16, 256, B + 8, 0x30000, 1, None), -4),   # misaligned x
+    ((A, gq.Q4_K, 16, 256, B, B + 16, 1, None), -3),        # y overlaps x
+    ((A, gq.Q4_K, 16, 256, B, A + 32, 1, None), -3),        # y overlaps blob
+    ((A, gq.Q4_K, 1 << 31, 256, B, 0x30000, 1, None), -5),  # rows too large
+    ((A, gq.Q4_K, 16, 32768, B, 0x30000, 1, None), -5),     # cols beyond GEMV LDS limit
+])
+def test_matmul_validation(args, code):
+    assert gq.lib().gq_matmul(*args) == code
+
+
+def test_matmul_zero_tokens_is_noop():
+    # n_tok = 0 succeeds without touching any pointer
+    assert gq.lib().gq_matmul(None, gq.Q4_K, 16, 256, None, None, 0, None) == 0
+
+
+def test_matmul_ex_bad_x_type():
+    assert gq.lib().gq_matmul_ex(A, gq.Q4_K, 16, 256, B, gq.Q8_0, 0x30000, 1, None) == -1
+
+
+def test_dequant_and_quantize_validation():
+    L = gq.lib()
+    assert L.gq_dequant(A, gq.Q6_K, 4, 255, B, gq.F32, None) == -2
+    assert L.gq_dequant(A, gq.Q6_K, 4, 256, B, gq.Q4_0, None) == -1
+    assert L.gq_dequant(A, gq.Q6_K, 4, 256, A + 16, gq.F32, None) == -3
+    assert L.gq_dequant(A, gq.Q6_K, 4, 256, B + 2, gq.F16, None) == -4
+    assert L.gq_quantize(A, gq.Q4_K, 4, 200, B, None) == -2
+    assert L.gq_quantize(None, gq.Q4_K, 4, 256, B, None) == -3
+    assert L.gq_quantize(A, gq.Q4_K, 4, 256, A + 64, None) == -3

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (stated in the design notes):
+  * dequantization and quantization: bit-exact (NaN compared as NaN);
+  * GEMV / matmul: |y_gpu - y_ref| <= 1e-3 * sum_c |w^[r,c] * x[t,c]| for every
+    output, with y_ref the oracle's fp64 dequant-then-dot.
+Every input is seeded (synth.py).  Blobs come from the oracle's quantizer
+unless a test checks the GPU quantizer itself.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gguf_quant_matmul_amd as gq
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256}
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
+TOL = 1e-3
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def check_matmul(y_gpu, blob, t, rows, cols, x, rows_idx=None, label=""):
+    """Compare y_gpu [n, rows] (numpy) with the oracle on all or sampled rows."""
+    if rows_idx is None:
+        ref, rabs = oracle.matmul_f64(blob, t, rows, cols, x, threads=THREADS)
+        got = y_gpu.astype(np.float64)
+    else:
+        rb = oracle.row_bytes(t, cols)
+        sub = blob.reshape(rows, rb)[rows_idx].reshape(-1)
+        ref, rabs = oracle.matmul_f64(sub, t, len(rows_idx), cols, x, threads=THREADS)
+        got = y_gpu[:, rows_idx].astype(np.float64)
+    err = np.abs(got - ref)
+    ratio = float(np.max(err / np.maximum(rabs, 1e-300)))
+    say(f"  {label} max |err| / sum|w*x| = {ratio:.3e}")
+    bad = ~(err <= TOL * rabs)
+    assert not bad.any(), f"{label}: {int(bad.sum())} outputs beyond tolerance, worst ratio {ratio:.3e}"
+    return ratio
+
+
+def quantized(t, rows, cols, seed, outliers=0.01):
+    w = synth.weights(rows, cols, seed=seed, outlier_frac=outliers)
+    return w, oracle.quantize(w, t)
+
+
+# ---------------------------------------------------------------- dequant / quantize
+
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+def test_dequant_bit_exact(t):
+    rows, cols = 37, 3 * QK[t]
+    say(f"dequant {t} {rows}x{cols}")
+    _, blob = quantized(t, rows, cols, seed=11)
+    bd = to_dev(blob)
+    y32 = gq.dequant(bd, t, rows, cols).cpu().numpy()
+    y16 = gq.dequant(bd, t, rows, cols, dtype=torch.float16).cpu().numpy()
+    ref = oracle.dequant_f32(blob, t, rows, cols)
+    assert np.array_equal(y32.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(y16.view(np.uint16), ref.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+def test_dequant_fuzz_bytes(t):
+    """Random bytes: every field pattern, including NaN/Inf/subnormal scales."""
+    rows, cols = 64, 4 * QK[t]
+    say(f"dequant fuzz {t}")
+    blob = synth.random_bytes(rows * oracle.row_bytes(t, cols), seed=5)
+    y = gq.dequant(to_dev(blob), t, rows, cols).cpu().numpy()
+    ref = oracle.dequant_f32(blob, t, rows, cols)
+    both_nan = np.isnan(y) & np.isnan(ref)
+    same = y.view(np.uint32) == ref.view(np.uint32)
+    assert np.all(both_nan | same)
+
+
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+def test_quantize_bit_exact(t):
+    rows, cols = 50, 3 * QK[t]
+    say(f"quantize {t}")
+    w = synth.weights(rows, cols, seed=21, outlier_frac=0.02)
+    # special rows: zeros, constant, all positive, all negative, tiny (fp16
+    # subnormal scales), huge (saturating scales)
+    w[0] = 0.0
+    w[1] = 0.0312
+    w[2] = np.abs(w[2])
+    w[3] = -np.abs(w[3])
+    w[4] *= 1e-5
+    w[5] *= 1e7
+    blob = gq.quantize(to_dev(w), t).cpu().numpy()
+    ref = oracle.quantize(w, t)
+    assert np.array_equal(blob, ref), f"{int((blob != ref).sum())} bytes differ"
+
+
+# ---------------------------------------------------------------- GEMV (n = 1)
+
+GEMV_SHAPES = {
+    "q4_k": [(1, 256), (37, 2304), (257, 4096), (130, 16384)],
+    "q6_k": [(1, 256), (37, 2304), (257, 11008), (64, 14336)],
+    "q8_0": [(1, 32), (37, 96), (257, 4096), (33, 2080)],
+    "q5_0": [(1, 32), (37, 96), (257, 4096), (33, 2080)],
+    "q4_0": [(1, 32), (37, 96), (257, 4096), (33, 2080)],
+}
+
+
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+@pytest.mark.parametrize("xdt", ["f32", "f16"])
+def test_gemv_parity(t, xdt):
+    for i, (rows, cols) in enumerate(GEMV_SHAPES[t]):
+        say(f"gemv {t} {rows}x{cols} x={xdt}")
+        _, blob = quantized(t, rows, cols, seed=100 + i)
+        x = synth.activations(1, cols, seed=200 + i, dtype=xdt)
+        y = gq.matmul(to_dev(blob), t, rows, cols, to_dev(x)).cpu().numpy()
+        check_matmul(y, blob, t, rows, cols, x, label=f"{t} {rows}x{cols} {xdt}")
+
+
+# ---------------------------------------------------------------- matrix cores (n >= 2)
+
+MM_SHAPES = {"q4_k": (75, 512), "q6_k": (75, 768), "q8_0": (75, 352), "q5_0": (75, 288),
+             "q4_0": (75, 320)}
+
+
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+@pytest.mark.parametrize("xdt", ["f16", "f32"])
+def test_mfma_parity(t, xdt):
+    rows, cols = MM_SHAPES[t]
+    _, blob = quantized(t, rows, cols, seed=31)
+    bd = to_dev(blob)
+    for n in (2, 7, 16, 33, 64, 100, 130):
+        say(f"mfma {t} {rows}x{cols} n={n} x={xdt}")
+        x = synth.activations(n, cols, seed=40 + n, dtype=xdt)
+        y = gq.matmul(bd, t, rows, cols, to_dev(x)).cpu().numpy()
+        check_matmul(y, blob, t, rows, cols, x, label=f"{t} n={n} {xdt}")
+
+
+def test_mfma_many_slabs_and_rows():
+    t, rows, cols = "q4_k", 300, 4096
+    _, blob = quantized(t, rows, cols, seed=32)
+    x = synth.activations(40, cols, seed=33, dtype="f16")
+    say("mfma q4_k 300x4096 n=40")
+    y = gq.matmul(to_dev(blob), t, rows, cols, to_dev(x)).cpu().numpy()
+    check_matmul(y, blob, t, rows, cols, x, label="q4_k 300x4096 n=40")
+
+
+# ---------------------------------------------------------------- exact special cases
+
+def _q8_unit_blob(codes):
+    rows, cols = codes.shape
+    blocks = codes.reshape(rows, cols // 32, 32).astype(np.int8).view(np.uint8)
+    head = np.zeros((rows, cols // 32, 2), dtype=np.uint8)
+    head[..., 1] = 0x3C                                  # d = 1.0
+    return np.concatenate([head, blocks], axis=2).reshape(-1)
+
+
+@pytest.mark.parametrize("n", [1, 9])
+def test_integer_reduction_exact(n):
+    """Q8_0 with d = 1 and small-integer x is an exact integer product."""
+    rng = np.random.default_rng(3)
+    rows, cols = 70, 512
+    codes = rng.integers(-128, 128, size=(rows, cols))
+    xi = rng.integers(-16, 17, size=(n, cols))
+    blob = _q8_unit_blob(codes)
+    say(f"integer reduction n={n}")
+    x = xi.astype(np.float16) if n > 1 else xi.astype(np.float32)
+    y = gq.matmul(to_dev(blob), "q8_0", rows, cols, to_dev(x)).cpu().numpy()
+    assert np.array_equal(y.astype(np.int64), xi @ codes.T)
+
+
+@pytest.mark.parametrize("xdt", ["f16", "f32"])
+@pytest.mark.parametrize("n", [1, 3, 40])
+def test_identity_reduction(n, xdt):
+    """Q8_0 with d = 1 and one code 1 per row (row r picks column r): y = x.
+    Exact for fp16 x; fp32 x at n >= 2 is split into two fp16 parts, which
+    keeps all but the last 2 bits of the fp32 significand."""
+    rows = cols = 256
+    codes = np.eye(rows, cols, dtype=np.int64)
+    x = synth.activations(n, cols, seed=90 + n, dtype=xdt)
+    say(f"identity n={n} x={xdt}")
+    y = gq.matmul(to_dev(_q8_unit_blob(codes)), "q8_0", rows, cols, to_dev(x)).cpu().numpy()
+    xs = x.astype(np.float64)
+    if xdt == "f16" or n == 1:
+        assert np.array_equal(y.astype(np.float64), xs)
+    else:
+        assert np.all(np.abs(y - xs) <= 2.0 ** -21 * np.abs(xs) + 2.0 ** -25)
+
+
+def _scale_by_two(blob, t, rows, cols):
+    qk, bb = oracle.block_info(t)
+    b = blob.copy().reshape(-1, bb)
+    offs = [0, 2] if t == "q4_k" else [0]
+    for off in offs:
+        h = b[:, off].astype(np.uint16) | (b[:, off + 1].astype(np.uint16) << 8)
+        mag = h & 0x7FFF
+        assert np.all((mag >> 10) < 30)
+        h = np.where(mag >= 0x0400, h + 0x0400, (h & 0x8000) | (mag << 1)).astype(np.uint16)
+        b[:, off] = (h & 0xFF).astype(np.uint8)
+        b[:, off + 1] = (h >> 8).astype(np.uint8)
+    return b.reshape(-1)
+
+
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+def test_power_of_two_scaling_is_exact(t):
+    """Doubling every fp16 scale doubles y bit for bit, at any summation order."""
+    rows, cols = 64, 2 * QK[t] if QK[t] == 256 else 256
+    _, blob = quantized(t, rows, cols, seed=55)
+    b2 = _scale_by_two(blob, t, rows, cols)
+    for n, xdt in ((1, "f32"), (20, "f16")):
+        say(f"pow2 {t} n={n}")
+        x = to_dev(synth.activations(n, cols, seed=56, dtype=xdt))
+        y1 = gq.matmul(to_dev(blob), t, rows, cols, x).cpu().numpy()
+        y2 = gq.matmul(to_dev(b2), t, rows, cols, x).cpu().numpy()
+        assert np.array_equal(y2, 2 * y1)
+
+
+def test_deterministic_run_to_run():
+    t, rows, cols = "q6_k", 4096, 4096
+    _, blob = quantized(t, rows, cols, seed=60)
+    bd = to_dev(blob)
+    for n, xdt in ((1, "f32"), (64, "f16")):
+        say(f"determinism n={n}")
+        x = to_dev(synth.activations(n, cols, seed=61, dtype=xdt))
+        a = gq.matmul(bd, t, rows, cols, x).cpu().numpy()
+        b = gq.matmul(bd, t, rows, cols, x).cpu().numpy()
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_nan_scale_propagates():
+    t, rows, cols = "q4_k", 16, 512
+    _, blob = quantized(t, rows, cols, seed=70)
+    blob = blob.copy()
+    rb = oracle.row_bytes(t, cols)
+    blob[3 * rb + 144 + 0] = 0x00
+    blob[3 * rb + 144 + 1] = 0x7E                         # d of row 3, block 1 = NaN
+    for n, xdt in ((1, "f32"), (5, "f16")):
+        say(f"nan propagation n={n}")
+        x = to_dev(synth.activations(n, cols, seed=71, dtype=xdt))
+        y = gq.matmul(to_dev(blob), t, rows, cols, x).cpu().numpy()
+        assert np.all(np.isnan(y[:, 3]))
+        assert np.all(np.isfinite(np.delete(y, 3, axis=1)))
+
+
+def test_zero_tokens_and_tiny():
+    t = "q4_k"
+    _, blob = quantized(t, 1, 256, seed=80)
+    bd = to_dev(blob)
+    say("zero tokens")
+    out = torch.empty((0, 1), dtype=torch.float32, device=dev())
+    x = torch.zeros((0, 256), dtype=torch.float32, device=dev())
+    assert gq.lib().gq_matmul(bd.data_ptr(), gq.Q4_K, 1, 256, x.data_ptr(), out.data_ptr(), 0, None) == 0
+    x1 = synth.activations(1, 256, seed=81)
+    y = gq.matmul(bd, t, 1, 256, to_dev(x1)).cpu().numpy()
+    check_matmul(y, blob, t, 1, 256, x1, label="1x256")
