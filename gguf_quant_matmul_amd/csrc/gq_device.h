@@ -48,11 +48,21 @@ __device__ __forceinline__ float h2f(uint32_t h) {
   return (float)v;
 }
 
-// Byte k of w as an exact fp32 (compiles to v_cvt_f32_ubyte{k}).
-__device__ __forceinline__ float ub0(uint32_t w) { return (float)(w & 0xFFu); }
-__device__ __forceinline__ float ub1(uint32_t w) { return (float)((w >> 8) & 0xFFu); }
-__device__ __forceinline__ float ub2(uint32_t w) { return (float)((w >> 16) & 0xFFu); }
-__device__ __forceinline__ float ub3(uint32_t w) { return (float)(w >> 24); }
+// Byte k of w as an exact fp32: one v_cvt_f32_ubyte{k}.  Written as asm
+// because the compiler otherwise folds a preceding nibble mask into a
+// v_bfe_u32 + v_cvt_f32_ubyte0 pair.
+__device__ __forceinline__ float ub0(uint32_t w) {
+  float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(w)); return r;
+}
+__device__ __forceinline__ float ub1(uint32_t w) {
+  float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(w)); return r;
+}
+__device__ __forceinline__ float ub2(uint32_t w) {
+  float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(w)); return r;
+}
+__device__ __forceinline__ float ub3(uint32_t w) {
+  float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(w)); return r;
+}
 
 // Byte k of w as a signed (two's complement) exact fp32 (v_cvt_f32_i32 with
 // a sign-extending byte select).
@@ -109,6 +119,42 @@ __device__ __forceinline__ uint32_t q6k_hi(uint32_t hq, int u) {
 __device__ __forceinline__ uint32_t spread4_bit4(uint32_t v) {
   v &= 0xFu;
   return ((v & 1u) << 4) | ((v & 2u) << 11) | ((v & 4u) << 18) | ((v & 8u) << 25);
+}
+
+// Wave-uniform value in a scalar register.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Wave64 sum on the DPP network (no LDS round trips): quad swaps, then row
+// shifts by 4 and 8, then the row broadcasts; lane 63 ends with the total,
+// which readlane returns to every lane.  Lanes a DPP source does not cover
+// contribute the 0 passed as the old value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x114>(v);   // row_shr:4
+  v += dpp_mov<0x118>(v);   // row_shr:8
+  v += dpp_mov<0x142>(v);   // row_bcast:15
+  v += dpp_mov<0x143>(v);   // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over each aligned group of G lanes (G = 16, 32 or 64) on the DPP
+// network; the group's total lands in its last lane (lane G-1 of the group).
+template <int G>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(G == 16 || G == 32 || G == 64, "group of 16, 32 or 64 lanes");
+  v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x114>(v);   // row_shr:4
+  v += dpp_mov<0x118>(v);   // row_shr:8: lanes 12..15 of each row hold its sum
+  if (G >= 32) v += dpp_mov<0x142>(v);   // row_bcast:15: row pairs
+  if (G >= 64) v += dpp_mov<0x143>(v);   // row_bcast:31: whole wave
+  return v;
 }
 
 // Wave64 sum with cross-lane swaps (result valid in every lane).

@@ -1,264 +1,361 @@
 // k_gemv.hip — batch-1 GEMV over GGUF blocks, dequantized inside the dot
 // product ("Local LLM inference", "The mmap backend").  Decode at batch 1
 // reads every weight once and is bound by memory bandwidth ("12 — llama.cpp /
-// GGUF", "The bandwidth cap"), so the kernel is built around the weight
-// stream:
-//   * lane <-> 32-weight segment of a row; consecutive lanes read consecutive
-//     16-byte pieces of the same row, so a wave load covers ~1 KB of the blob;
-//   * each wave keeps R rows in flight and reuses one x segment (held in
-//     registers) for all of them;
-//   * x lives in LDS as fp32 (16-byte chunks XOR-swizzled per segment so the
-//     64 lanes' 16-byte reads hit distinct banks);
-//   * per-segment sums are factored: Q4_K computes a*sum(q*x) - b*sum(x), from
-//     w = (d*sc)*q - dmin*m of Hitchhiker's Guide §11.2, which removes the
-//     per-weight scale and min operations; the other types convert each code
-//     to the signed integer q - offset first, so every product is exact
-//     relative to w; fp32 accumulation throughout.
+// GGUF", "The bandwidth cap"); on gfx950 the vector-ALU instruction count per
+// weight is the second limit, so the kernel keeps it near the essential
+// convert + FMA per weight:
+//   * lane <-> one 64-weight slice of a row (a quarter of a Q4_K/Q6_K block,
+//     or two 32-weight blocks), so block headers are decoded once per 64
+//     weights;
+//   * weights arrive through buffer loads on a per-row-set scalar descriptor:
+//     the per-lane byte offset is loop-invariant, so no address arithmetic
+//     runs per load, and reads past the descriptor's range return zero;
+//   * x is staged once per workgroup in LDS as fp32 (16-byte chunks XOR-
+//     swizzled per slice) with the sums of x over every 16 columns;
+//   * Q4_K and Q6_K use factored sub-block sums a*sum(q*x) - b*sum(x)
+//     (Hitchhiker's Guide §11.2, w = (d*sc)*q - dmin*m; for Q6_K the offset
+//     32 plays the min); the 32-weight types convert each code to the signed
+//     q - offset so every product is exact relative to w; fp32 accumulation;
+//   * persistent workgroups (as many as fit on the chip) loop over groups of
+//     rows with the next group's loads in flight; row sums use the DPP network.
 #include "gq_device.h"
 #include "gq_launch.h"
 
 namespace gq {
 
-// Raw bytes of one segment and its header, and the factored segment dot.
-template <int T> struct Seg;
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer resource word 3 (gfx950)
 
-template <> struct Seg<GQ_Q4_K> {
-  u32x4 qs, hd;
-  __device__ void load(const uint8_t* row, int s) {
-    const uint8_t* b = row + (size_t)(s >> 3) * 144;
-    hd = ld16a(b);
-    qs = ld16a(b + 16 + 16 * (s & 7));
-  }
-  __device__ void zero() { qs = u32x4{0, 0, 0, 0}; hd = u32x4{0, 0, 0, 0}; }
-  __device__ float dot(const float* x, float xs0, float xs1, int s) const {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
-      a0 = fmaf(ub0(lo), x[4 * j + 0], a0);
-      a0 = fmaf(ub1(lo), x[4 * j + 1], a0);
-      a0 = fmaf(ub2(lo), x[4 * j + 2], a0);
-      a0 = fmaf(ub3(lo), x[4 * j + 3], a0);
-      a1 = fmaf(ub0(hi), x[16 + 4 * j + 0], a1);
-      a1 = fmaf(ub1(hi), x[16 + 4 * j + 1], a1);
-      a1 = fmaf(ub2(hi), x[16 + 4 * j + 2], a1);
-      a1 = fmaf(ub3(hi), x[16 + 4 * j + 3], a1);
-    }
-    uint32_t p = q4k_pair(hd.y, hd.z, hd.w, s & 7);
-    float a = h2f(hd.x) * (float)(p & 63u);
-    float b = h2f(hd.x >> 16) * (float)(p >> 6);
-    return a * (a0 + a1) - b * (xs0 + xs1);
-  }
-};
-
-template <> struct Seg<GQ_Q6_K> {
-  u32x4 ql;
-  u32x2 qh;
-  uint32_t sc, d;
-  __device__ void load(const uint8_t* row, int s) {
-    const uint8_t* b = row + (size_t)(s >> 3) * 210;
-    const int g = s & 7;
-    ql = ld16u(b + 18 + 16 * g);
-    qh = ld8u(b + 146 + 8 * g);
-    sc = ld2u(b + 2 + 2 * g);
-    d = ld2u(b);
-  }
-  __device__ void zero() { ql = u32x4{0, 0, 0, 0}; qh = u32x2{0, 0}; sc = 0; d = 0; }
-  __device__ float dot(const float* x, float, float, int) const {
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t h = (j & 1) ? qh.y : qh.x;
-      // signed codes q - 32 per byte, so each product is exact relative to w
-      uint32_t lo = centre<32>((ql[j] & 0x0F0F0F0Fu) | q6k_hi(h, j >> 1));
-      uint32_t hi = centre<32>(((ql[j] >> 4) & 0x0F0F0F0Fu) | q6k_hi(h, 2 + (j >> 1)));
-      s0 = fmaf(sb0(lo), x[4 * j + 0], s0);
-      s0 = fmaf(sb1(lo), x[4 * j + 1], s0);
-      s0 = fmaf(sb2(lo), x[4 * j + 2], s0);
-      s0 = fmaf(sb3(lo), x[4 * j + 3], s0);
-      s1 = fmaf(sb0(hi), x[16 + 4 * j + 0], s1);
-      s1 = fmaf(sb1(hi), x[16 + 4 * j + 1], s1);
-      s1 = fmaf(sb2(hi), x[16 + 4 * j + 2], s1);
-      s1 = fmaf(sb3(hi), x[16 + 4 * j + 3], s1);
-    }
-    float c0 = sb0(sc), c1 = sb1(sc);
-    return h2f(d) * (c0 * s0 + c1 * s1);
-  }
-};
-
-template <> struct Seg<GQ_Q8_0> {
-  u32x4 c0, c1;
-  uint32_t d;
-  __device__ void load(const uint8_t* row, int s) {
-    const uint8_t* b = row + (size_t)s * 34;
-    d = ld2u(b);
-    c0 = ld16u(b + 2);
-    c1 = ld16u(b + 18);
-  }
-  __device__ void zero() { c0 = u32x4{0, 0, 0, 0}; c1 = c0; d = 0; }
-  __device__ float dot(const float* x, float, float, int) const {
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      a0 = fmaf(sb0(c0[j]), x[4 * j + 0], a0);
-      a0 = fmaf(sb1(c0[j]), x[4 * j + 1], a0);
-      a0 = fmaf(sb2(c0[j]), x[4 * j + 2], a0);
-      a0 = fmaf(sb3(c0[j]), x[4 * j + 3], a0);
-      a1 = fmaf(sb0(c1[j]), x[16 + 4 * j + 0], a1);
-      a1 = fmaf(sb1(c1[j]), x[16 + 4 * j + 1], a1);
-      a1 = fmaf(sb2(c1[j]), x[16 + 4 * j + 2], a1);
-      a1 = fmaf(sb3(c1[j]), x[16 + 4 * j + 3], a1);
-    }
-    return h2f(d) * (a0 + a1);
-  }
-};
-
-// Q4_0 and Q5_0: low nibbles are elements 0..15, high nibbles 16..31
-// ("How LLM Inference Engines Work", "Loading GGUF Models"); Q5_0 adds bit 4.
-template <int T> struct SegQ40Q50 {
-  static constexpr bool Q5 = (T == GQ_Q5_0);
-  u32x4 qs;
-  uint32_t qh, d;
-  __device__ void load(const uint8_t* row, int s) {
-    const uint8_t* b = row + (size_t)s * (Q5 ? 22 : 18);
-    d = ld2u(b);
-    qh = Q5 ? ld4u(b + 2) : 0u;
-    qs = ld16u(b + (Q5 ? 6 : 2));
-  }
-  __device__ void zero() { qs = u32x4{0, 0, 0, 0}; qh = 0; d = 0; }
-  __device__ float dot(const float* x, float, float, int) const {
-    constexpr int OFF = Q5 ? 16 : 8;
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      uint32_t lo = qs[j] & 0x0F0F0F0Fu, hi = (qs[j] >> 4) & 0x0F0F0F0Fu;
-      if (Q5) {
-        lo |= spread4_bit4(qh >> (4 * j));
-        hi |= spread4_bit4(qh >> (16 + 4 * j));
-      }
-      lo = centre<OFF>(lo);
-      hi = centre<OFF>(hi);
-      a0 = fmaf(sb0(lo), x[4 * j + 0], a0);
-      a0 = fmaf(sb1(lo), x[4 * j + 1], a0);
-      a0 = fmaf(sb2(lo), x[4 * j + 2], a0);
-      a0 = fmaf(sb3(lo), x[4 * j + 3], a0);
-      a1 = fmaf(sb0(hi), x[16 + 4 * j + 0], a1);
-      a1 = fmaf(sb1(hi), x[16 + 4 * j + 1], a1);
-      a1 = fmaf(sb2(hi), x[16 + 4 * j + 2], a1);
-      a1 = fmaf(sb3(hi), x[16 + 4 * j + 3], a1);
-    }
-    return h2f(d) * (a0 + a1);
-  }
-};
-template <> struct Seg<GQ_Q4_0> : SegQ40Q50<GQ_Q4_0> {};
-template <> struct Seg<GQ_Q5_0> : SegQ40Q50<GQ_Q5_0> {};
-
-// Physical float index in LDS of logical x index f (16-byte chunks of each
-// 32-float segment XOR-swizzled by the segment index).
-__device__ __forceinline__ int xswz(int f) {
-  int sg = f >> 5, c = (f >> 2) & 7;
-  return (sg << 5) | ((c ^ (sg & 7)) << 2) | (f & 3);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + imm, 0, 0));
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff + imm, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff + imm, 0, 0);
 }
 
-template <int T, bool XF16, int R>
+// acc + sum over the 4 bytes of w of (byte as unsigned / signed) * x[k]
+__device__ __forceinline__ float dot4u(uint32_t w, const float* x, float acc) {
+  acc = fmaf(ub0(w), x[0], acc);
+  acc = fmaf(ub1(w), x[1], acc);
+  acc = fmaf(ub2(w), x[2], acc);
+  return fmaf(ub3(w), x[3], acc);
+}
+__device__ __forceinline__ float dot4s(uint32_t w, const float* x, float acc) {
+  acc = fmaf(sb0(w), x[0], acc);
+  acc = fmaf(sb1(w), x[1], acc);
+  acc = fmaf(sb2(w), x[2], acc);
+  return fmaf(sb3(w), x[3], acc);
+}
+
+// One lane's 64-weight slice of one row: raw registers and the slice dot in
+// two halves of 32 weights.  voff(sl) is slice sl's byte offset in its row;
+// j = sl % 4 its quarter of a K-quant block.  dot(h, x, xs, j) takes half h's
+// 32 activations and the sums of x over its two 16-column quarters.  A final
+// slice of a 32-weight type may have only its first block in the row; its
+// second half is then never computed.
+template <int T> struct Slice;
+
+template <> struct Slice<GQ_Q4_K> {           // sub-blocks 2j, 2j+1 of a super-block
+  u32x4 hd, q0, q1;
+  static __device__ int voff(int sl) { return (sl >> 2) * 144; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int j) {
+    hd = bld16(r, vo, 0);
+    q0 = bld16(r, vo + 32 * j, 16);
+    q1 = bld16(r, vo + 32 * j, 32);
+  }
+  __device__ float dot(int h, const float* x, const float* xs, int j) const {
+    const u32x4 q = h ? q1 : q0;              // sub-block 2j + h
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {             // low nibbles: elements 4k.., high: 16+4k..
+      s = dot4u(q[k] & 0x0F0F0F0Fu, x + 4 * k, s);
+      t = dot4u((q[k] >> 4) & 0x0F0F0F0Fu, x + 16 + 4 * k, t);
+    }
+    // (scale, min) of sub-blocks 2j, 2j+1: the 24 bits at bit 24j of the
+    // 96-bit field stream in header bytes 4..15
+    const uint32_t lo = (j <= 1) ? hd.y : (j == 2) ? hd.z : hd.w;
+    const uint32_t hi = (j <= 1) ? hd.z : hd.w;
+    const uint32_t f = __builtin_amdgcn_alignbit(hi, lo, (24 * j) & 31) >> (12 * h);
+    const float a = h2f(hd.x) * (float)(f & 63u);
+    const float b = h2f(hd.x >> 16) * (float)((f >> 6) & 63u);
+    return fmaf(a, s + t, -b * (xs[0] + xs[1]));
+  }
+};
+
+template <> struct Slice<GQ_Q6_K> {           // 32-weight groups 2j, 2j+1
+  u32x4 l0, l1, h;
+  uint32_t sc, d;
+  static __device__ int voff(int sl) { return (sl >> 2) * 210; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int j) {
+    l0 = bld16(r, vo + 32 * j, 18);
+    l1 = bld16(r, vo + 32 * j, 34);
+    h = bld16(r, vo + 16 * j, 146);
+    sc = bld4(r, vo + 4 * j, 2);
+    d = bld2(r, vo, 0);
+  }
+  __device__ float dot(int g, const float* x, const float* xs, int) const {
+    // group 2j + g; unsigned codes q = low4 | high2 << 4; per 16-weight
+    // quarter sum((q - 32) * x) = sum(q * x) - 32 * sum(x)
+    const u32x4 L = g ? l1 : l0;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t H = h[2 * g + (k & 1)];
+      const uint32_t lo = (L[k] & 0x0F0F0F0Fu) | q6k_hi(H, k >> 1);
+      const uint32_t hi = ((L[k] >> 4) & 0x0F0F0F0Fu) | q6k_hi(H, 2 + (k >> 1));
+      s0 = dot4u(lo, x + 4 * k, s0);
+      s1 = dot4u(hi, x + 16 + 4 * k, s1);
+    }
+    const uint32_t sc2 = sc >> (16 * g);
+    const float r = fmaf(sb1(sc2), fmaf(-32.f, xs[1], s1), sb0(sc2) * fmaf(-32.f, xs[0], s0));
+    return h2f(d) * r;
+  }
+};
+
+template <> struct Slice<GQ_Q8_0> {           // blocks 2*sl, 2*sl+1
+  u32x4 c[4];
+  uint32_t d0, d1;
+  static __device__ int voff(int sl) { return sl * 68; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int) {
+    d0 = bld2(r, vo, 0);
+    c[0] = bld16(r, vo, 2);
+    c[1] = bld16(r, vo, 18);
+    d1 = bld2(r, vo, 34);
+    c[2] = bld16(r, vo, 36);
+    c[3] = bld16(r, vo, 52);
+  }
+  __device__ float dot(int h, const float* x, const float*, int) const {
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      a = dot4s(c[2 * h][k], x + 4 * k, a);
+      b = dot4s(c[2 * h + 1][k], x + 16 + 4 * k, b);
+    }
+    return h2f(h ? d1 : d0) * (a + b);
+  }
+};
+
+// Q4_0 and Q5_0: low nibbles are elements 0..15 of a block, high nibbles
+// 16..31 ("How LLM Inference Engines Work", "Loading GGUF Models"); Q5_0 adds
+// a fifth bit per element from a 32-bit word.
+template <int T> struct SliceQ40Q50 {
+  static constexpr bool Q5 = (T == GQ_Q5_0);
+  static constexpr int BB = Q5 ? 22 : 18;
+  static constexpr int OFF = Q5 ? 16 : 8;
+  u32x4 q0, q1;
+  uint32_t d0, d1, h0, h1;
+  static __device__ int voff(int sl) { return sl * 2 * BB; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int) {
+    d0 = bld2(r, vo, 0);
+    d1 = bld2(r, vo, BB);
+    q0 = bld16(r, vo, Q5 ? 6 : 2);
+    q1 = bld16(r, vo, BB + (Q5 ? 6 : 2));
+    h0 = Q5 ? bld4(r, vo, 2) : 0u;
+    h1 = Q5 ? bld4(r, vo, BB + 2) : 0u;
+  }
+  __device__ float dot(int h, const float* x, const float*, int) const {
+    const u32x4 q = h ? q1 : q0;
+    const uint32_t qh = h ? h1 : h0;
+    float a = 0.f, b = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      uint32_t lo = q[k] & 0x0F0F0F0Fu, hi = (q[k] >> 4) & 0x0F0F0F0Fu;
+      if (Q5) {
+        lo |= spread4_bit4(qh >> (4 * k));
+        hi |= spread4_bit4(qh >> (16 + 4 * k));
+      }
+      a = dot4s(centre<OFF>(lo), x + 4 * k, a);
+      b = dot4s(centre<OFF>(hi), x + 16 + 4 * k, b);
+    }
+    return h2f(h ? d1 : d0) * (a + b);
+  }
+};
+template <> struct Slice<GQ_Q4_0> : SliceQ40Q50<GQ_Q4_0> {};
+template <> struct Slice<GQ_Q5_0> : SliceQ40Q50<GQ_Q5_0> {};
+
+// Physical float index in LDS of logical x index f: 16-byte chunk c of slice
+// s lands at chunk c ^ (s & 15), so 16 lanes reading chunk c of 16
+// consecutive slices hit 16 distinct groups of 4 banks.
+__device__ __forceinline__ int xswz(int f) {
+  const int s = f >> 6, c = (f >> 2) & 15;
+  return (s << 6) | ((c ^ (s & 15)) << 2) | (f & 3);
+}
+
+// Persistent GEMV.  LPR lanes cover a row's slices in each of npass passes
+// (a wave holds 64/LPR rows side by side when rows are short); each wave takes
+// R such row sets per group and walks its groups pass by pass, so the double
+// buffer holds one pass whatever the row length.
+template <int T, bool XF16, int LPR, int R, int XPT>
 __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, int rows,
-                                              int cols, int64_t rb, const void* __restrict__ xv,
+                                              int cols, int rb, const void* __restrict__ xv,
                                               float* __restrict__ y) {
-  extern __shared__ float xsm[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nseg = cols >> 5;
-  const int npass = (nseg + 63) >> 6;
-  const int r0 = (blockIdx.x * 4 + wave) * R;
+  extern __shared__ float xsm[];           // x padded to whole slices, then 16-column sums
+  constexpr int RPW = 64 / LPR;            // rows side by side in a wave
+  constexpr int ROWS = RPW * R;            // rows per group
+  // XPT = float4 of x staged per thread: cols <= XPT * 1024
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int nsl = (cols + 63) >> 6;        // slices per row (the last may be half)
+  const int npass = (nsl + LPR - 1) / LPR;
+  const int cpad = nsl << 6;
+  const int ngroups = (rows + ROWS - 1) / ROWS;
+  const int stride = gridDim.x * 4;
+  const int sub = lane / LPR;              // which of the side-by-side rows
+  const int li = lane % LPR;
 
-  const uint8_t* rowp[R];
+  // x from global first (clamped, unconditional loads), then the first pass's
+  // weights, then x into LDS: the LDS stores wait only for x
+  const int nc4 = cols >> 2;
+  f32x4 xr[XPT];
 #pragma unroll
-  for (int k = 0; k < R; k++) rowp[k] = blob + (int64_t)min(r0 + k, rows - 1) * rb;
-
-  // Issue the first pass's weight loads before staging x, so the HBM latency
-  // overlaps the LDS fill.
-  Seg<T> cur[R], nxt[R];
-  {
-    const int s = lane;
-#pragma unroll
-    for (int k = 0; k < R; k++) {
-      if (s < nseg) cur[k].load(rowp[k], s); else cur[k].zero();
+  for (int i = 0; i < XPT; i++) {
+    const int cc = min((int)threadIdx.x + 256 * i, nc4 - 1);
+    if constexpr (XF16) {
+      u32x2 hh = *reinterpret_cast<const u32x2*>((const _Float16*)xv + 4 * cc);
+      xr[i] = f32x4{h2f(hh.x), h2f(hh.x >> 16), h2f(hh.y), h2f(hh.y >> 16)};
+    } else {
+      xr[i] = reinterpret_cast<const f32x4*>(xv)[cc];
     }
   }
 
-  // Stage x (fp32) in LDS.
-  for (int c4 = threadIdx.x; c4 < (cols >> 2); c4 += 256) {
-    f32x4 v;
-    if constexpr (XF16) {
-      u32x2 h = *reinterpret_cast<const u32x2*>((const _Float16*)xv + 4 * c4);
-      v = f32x4{h2f(h.x), h2f(h.x >> 16), h2f(h.y), h2f(h.y >> 16)};
-    } else {
-      v = reinterpret_cast<const f32x4*>(xv)[c4];
+  Slice<T> cur[R], nxt[R];
+  // loads pass p of group grp into w; lanes past the row's last slice repeat
+  // it (their sums are dropped); the descriptor ends at the matrix's last row
+  auto load_item = [&](Slice<T> (&w)[R], int grp, int p) {
+    const int sl = min(p * LPR + li, nsl - 1);
+    const int vo = Slice<T>::voff(sl);
+#pragma unroll
+    for (int k = 0; k < R; k++) {
+      const int rw0 = uniform(grp * ROWS + k * RPW);
+      const int nr = max(0, min(RPW, rows - rw0));
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(blob + (int64_t)rw0 * rb, (uint32_t)(nr * rb));
+      w[k].load(rs, sub * rb + vo, sl & 3);
     }
-    *reinterpret_cast<f32x4*>(xsm + xswz(4 * c4)) = v;
+  };
+  int g = blockIdx.x * 4 + wave;
+  if (g < ngroups) load_item(cur, g, 0);
+
+  // x (fp32, zero-padded to whole slices) and its 16-column sums into LDS
+#pragma unroll
+  for (int i = 0; i < XPT; i++) {
+    const int c4 = (int)threadIdx.x + 256 * i;
+    if (c4 < (cpad >> 2))
+      *reinterpret_cast<f32x4*>(xsm + xswz(4 * c4)) = (c4 < nc4) ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+  float* xsum = xsm + cpad;
+  for (int q = threadIdx.x; q < (cpad >> 4); q += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(xsm + xswz((q << 4) + 4 * c));
+      s += (v.x + v.y) + (v.z + v.w);
+    }
+    xsum[q] = s;
   }
   __syncthreads();
 
-  float acc[R];
+  for (; g < ngroups; g += stride) {
+    float acc[R];
 #pragma unroll
-  for (int k = 0; k < R; k++) acc[k] = 0.f;
-
-  for (int p = 0; p < npass; p++) {
-    const int s = p * 64 + lane;
-    if (p + 1 < npass) {
-      const int sn = s + 64;
+    for (int k = 0; k < R; k++) acc[k] = 0.f;
+    for (int p = 0; p < npass; p++) {
+      // next item: this group's next pass, else the next group's first
+      const bool more = (p + 1 < npass) || (g + stride < ngroups);
+      if (more) {
+        if (p + 1 < npass) load_item(nxt, g, p + 1);
+        else load_item(nxt, g + stride, 0);
+      }
+      const int s0 = p * LPR + li;
+      const int s = min(s0, nsl - 1);
+      const bool live = s0 < nsl;
+      const bool second = (2 * s + 1) * 32 < cols;   // the slice's second half is in the row
 #pragma unroll
-      for (int k = 0; k < R; k++) {
-        if (sn < nseg) nxt[k].load(rowp[k], sn); else nxt[k].zero();
+      for (int h = 0; h < 2; h++) {
+        float x[32];
+        const float* base = xsm + (s << 6);
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(base + (((8 * h + c) ^ (s & 15)) << 2));
+          x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+        }
+        const float2 xs2 = *reinterpret_cast<const float2*>(xsum + 4 * s + 2 * h);
+        const float xs[2] = {xs2.x, xs2.y};
+        const bool use = live && (h == 0 || second);
+#pragma unroll
+        for (int k = 0; k < R; k++) {
+          const float d = cur[k].dot(h, x, xs, s & 3);
+          acc[k] += use ? d : 0.f;
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int k = 0; k < R; k++) cur[k] = nxt[k];
       }
     }
-    if (s < nseg) {
-      float x[32];
-      const float* base = xsm + (s << 5);
 #pragma unroll
-      for (int c = 0; c < 8; c++) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(base + ((c ^ (s & 7)) << 2));
-        x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
-      }
-      float xs0 = 0.f, xs1 = 0.f;            // segment sums: the Q4_K min term
-      if constexpr (T == GQ_Q4_K) {
-#pragma unroll
-        for (int e = 0; e < 16; e++) { xs0 += x[e]; xs1 += x[16 + e]; }
-      }
-#pragma unroll
-      for (int k = 0; k < R; k++) acc[k] += cur[k].dot(x, xs0, xs1, s);
+    for (int k = 0; k < R; k++) {
+      const float v = group_sum_dpp<LPR>(acc[k]);          // valid in lane LPR-1 of each group
+      const int r = g * ROWS + k * RPW + sub;
+      if (li == LPR - 1 && r < rows) y[r] = v;
     }
-    if (p + 1 < npass) {
-#pragma unroll
-      for (int k = 0; k < R; k++) cur[k] = nxt[k];
-    }
-  }
-
-#pragma unroll
-  for (int k = 0; k < R; k++) {
-    float v = wave_sum(acc[k]);
-    if (lane == k && r0 + k < rows) y[r0 + k] = v;
   }
 }
 
-template <int T, bool XF16, int R>
+#ifndef GQ_GEMV_R                 // row sets per wave when a row takes one pass
+#define GQ_GEMV_R 1
+#endif
+
+template <typename K>
+static int resident_wgs(K kern, size_t lds) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+  }
+  int per = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)kern, 256, lds) != hipSuccess ||
+      per < 1)
+    per = 1;
+  return cus * per;
+}
+
+template <int T, bool XF16, int LPR, int R, int XPT>
 static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, const void* x,
                               float* y, hipStream_t st) {
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
-  const size_t lds = (size_t)cols * 4;                 // cols <= 16384: at most 64 KB
-  auto kern = k_gemv<T, XF16, R>;
-  dim3 grid((unsigned)((rows + 4 * R - 1) / (4 * R)));
+  const int64_t cpad = (cols + 63) / 64 * 64;
+  const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4;   // <= 68 KB for cols <= 16384
+  auto kern = k_gemv<T, XF16, LPR, R, XPT>;
+  static size_t cap_lds = 0;               // resident workgroups for the last LDS size
+  static int cap = 0;
+  if (cap_lds != lds) { cap = resident_wgs(kern, lds); cap_lds = lds; }
+  const int64_t groups = (rows + (64 / LPR) * R - 1) / ((64 / LPR) * R);
+  const int64_t wgs = (groups + 3) / 4;
+  dim3 grid((unsigned)(wgs < cap ? wgs : cap));
   hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t*)blob, (int)rows, (int)cols,
-                     rb, x, y);
+                     (int)rb, x, y);
   return hipGetLastError();
 }
 
+// Shape dispatch: rows of up to 2048 weights share a wave (64/LPR of them);
+// longer rows take several passes of 64 slices.  Rows of up to 4096 weights
+// take R row sets per wave, longer ones one.
 template <int T, bool XF16>
 static hipError_t gemv_pick(const void* blob, int64_t rows, int64_t cols, const void* x, float* y,
                             hipStream_t st) {
-  // Enough workgroups to fill 256 CUs: fewer rows per wave on small matrices.
-  if (rows >= 8192) return gemv_launch<T, XF16, 4>(blob, rows, cols, x, y, st);
-  if (rows >= 2048) return gemv_launch<T, XF16, 2>(blob, rows, cols, x, y, st);
-  return gemv_launch<T, XF16, 1>(blob, rows, cols, x, y, st);
+  if (cols <= 1024) return gemv_launch<T, XF16, 16, GQ_GEMV_R, 4>(blob, rows, cols, x, y, st);
+  if (cols <= 2048) return gemv_launch<T, XF16, 32, GQ_GEMV_R, 4>(blob, rows, cols, x, y, st);
+  if (cols <= 4096) return gemv_launch<T, XF16, 64, GQ_GEMV_R, 4>(blob, rows, cols, x, y, st);
+  if (cols <= 8192) return gemv_launch<T, XF16, 64, 1, 8>(blob, rows, cols, x, y, st);
+  return gemv_launch<T, XF16, 64, 1, 16>(blob, rows, cols, x, y, st);
 }
 
 template <int T>
