@@ -1,35 +1,43 @@
 """Bench: Q4_K_M-mix GEMV effective weight bandwidth at batch 1 on one MI355X.
 
-A step is one pass of the decode-layer GEMVs of a Llama-7B-shaped layer in the
-Q4_K_M mix at batch 1 (q/k/v/o and ffn gate/up as Q4_K, ffn down as Q6_K,
-fp32 activations), i.e. every weight of the layer read once.  value = blob
-bytes of the layer / time per step, with the blobs resident in HBM.
+Workload: a Llama-7B-shaped decode layer in the Q4_K_M mix at batch 1 —
+q/k/v/o 4096x4096 and ffn gate/up 11008x4096 as Q4_K, ffn down 4096x11008 as
+Q6_K, fp32 activations.  As in decode engines, the projections that share an
+input are stored as one matrix (q|k|v: 12288x4096, gate|up: 22016x4096), so a
+step is four dependent GEMV launches (qkv, o, gate_up, down) that read every
+weight of the layer once.  value = layer blob bytes / time per step, with the
+blobs resident in HBM.
 
 Method:
-  * weights: synthetic N(0, 0.02^2) fp32 (synth.py), quantized on the GPU by
-    the library's own quantizer; x ~ N(0, 1) fp32;
-  * each step is replayed as a HIP graph of the 7 launches; steps rotate over
-    5 distinct copies of the layer (627 MB) so no step finds its weights in the
-    256 MB Infinity Cache;
-  * timed region: synchronize, K graph replays, synchronize (HIP events on the
-    replay stream);
-  * roofline: the dominant kernel (largest time per step) is timed live with
-    HIP events over graphs of back-to-back launches of that kernel alone,
+  * weights: synthetic N(0, 0.02^2) fp32, one seeded draw per original matrix,
+    quantized on the GPU by the library's quantizer; x ~ N(0, 1) fp32;
+  * each step is a HIP graph of the four launches; steps rotate over distinct
+    copies of the layer (>= 640 MB) so no step finds its weights in the 256 MB
+    Infinity Cache; timed region: synchronize, K graph replays, synchronize,
+    HIP events on the replay stream;
+  * roofline: the dominant kernel (largest time per step) timed live with HIP
+    events over graphs of 16 back-to-back launches of that kernel alone,
     rotating over >= 512 MB of copies; achieved = blob bytes per launch /
-    average launch duration against the 8 TB/s HBM peak;
-  * secondary: the Q4_K 11008x4096 dequant-GEMM at 512 fp16 tokens, GFLOP/s
-    against the 2.5 PFLOP/s dense fp16 matrix peak;
+    average launch duration, against the 8 TB/s HBM peak; traffic from the
+    committed counter summary when it was taken on the current kernel source;
+  * secondary: the Q4_K 11008x4096 dequant-GEMM at 512 fp16 tokens (GFLOP/s
+    against the 2.5 PFLOP/s dense fp16 matrix peak) and a sweep of the other
+    workload shapes;
   * cpu_baseline: the CPU oracle (fp64 dequant-then-dot, OpenMP over rows) on
     the same layer, the oracle quantizing its own blobs from the same draws.
 
-Prints one JSON line.
+Prints one JSON line.  `--profile-launches N` instead runs N plain (ungraphed)
+launches of each layer matrix plus a device copy of known size, for
+rocprofv3 kernel traces and counters.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -40,6 +48,17 @@ METRIC = "Q4_K_M GEMV effective weight GB/s (% HBM peak) at batch 1; GFLOP/s at 
 HBM_PEAK_GBS = 8000.0
 FP16_PEAK_TFLOPS = 2500.0
 CACHE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_decode_layer_counters.md")
+GEMV_SRC = os.path.join(ROOT, "gguf_quant_matmul_amd", "csrc", "k_gemv.hip")
+
+# (name, type, [(part, rows)], cols): parts are the original matrices, stored
+# one after another (row-major blobs concatenate row-wise).
+LAYER = [
+    ("qkv", "q4_k", [("attn_q", 4096), ("attn_k", 4096), ("attn_v", 4096)], 4096),
+    ("attn_o", "q4_k", [("attn_o", 4096)], 4096),
+    ("ffn_gate_up", "q4_k", [("ffn_gate", 11008), ("ffn_up", 11008)], 4096),
+    ("ffn_down", "q6_k", [("ffn_down", 4096)], 11008),
+]
 
 
 def log(msg):
@@ -52,46 +71,62 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
-    p.add_argument("--no-gemm", action="store_true", help="skip the 512-token GEMM line")
+    p.add_argument("--no-sweep", action="store_true", help="skip the secondary shapes")
+    p.add_argument("--profile-launches", type=int, default=0)
     return p.parse_args()
 
 
 class Mat:
-    def __init__(self, name, t, rows, cols, seed, ncopies):
+    """A (possibly fused) weight matrix on the GPU with rotating copies."""
+
+    def __init__(self, name, t, parts, cols, seed, ncopies, n_tok=1, x_dtype="f32", keep_w=False):
         import torch
         import gguf_quant_matmul_amd as gq
         import synth
-        self.name, self.t, self.rows, self.cols = name, t, rows, cols
+        self.name, self.t, self.cols = name, t, cols
+        self.rows = sum(r for _, r in parts)
         self.tid = gq.TYPES[t]
-        self.w = synth.weights(rows, cols, seed=seed)          # host fp32, kept for the oracle
-        wd = torch.from_numpy(self.w).cuda()
-        blob = gq.quantize(wd, t)
-        del wd
+        self.n_tok = n_tok
+        self.w = []
+        blobs = []
+        for i, (_, r) in enumerate(parts):
+            w = synth.weights(r, cols, seed=seed + i)
+            if keep_w:
+                self.w.append(w)
+            wd = torch.from_numpy(w).cuda()
+            blobs.append(gq.quantize(wd, t))
+            del wd
+        blob = torch.cat(blobs) if len(blobs) > 1 else blobs[0]
         self.bytes = blob.numel()
         self.copies = [blob] + [blob.clone() for _ in range(ncopies - 1)]
-        self.x = torch.from_numpy(synth.activations(1, cols, seed=seed + 1)).cuda()
-        self.y = torch.empty((1, rows), dtype=torch.float32, device="cuda")
+        x = synth.activations(n_tok, cols, seed=seed + 100, dtype=x_dtype)
+        self.x_host = x
+        self.x = torch.from_numpy(x).cuda()
+        self.xt = gq.F16 if x_dtype == "f16" else gq.F32
+        self.y = torch.empty((n_tok, self.rows), dtype=torch.float32, device="cuda")
 
-    def launch(self, copy, stream_ptr, n=1, x=None, y=None):
+    def ensure_copies(self, total_bytes):
+        need = max(2, -(-total_bytes // self.bytes))
+        while len(self.copies) < need:
+            self.copies.append(self.copies[0].clone())
+
+    def launch(self, copy, stream_ptr):
         import gguf_quant_matmul_amd as gq
-        x = self.x if x is None else x
-        y = self.y if y is None else y
-        xt = gq.F16 if x.dtype.itemsize == 2 else gq.F32
         rc = gq.lib().gq_matmul_ex(self.copies[copy % len(self.copies)].data_ptr(), self.tid,
-                                   self.rows, self.cols, x.data_ptr(), xt, y.data_ptr(), n,
-                                   stream_ptr)
+                                   self.rows, self.cols, self.x.data_ptr(), self.xt,
+                                   self.y.data_ptr(), self.n_tok, stream_ptr)
         if rc:
             raise RuntimeError(f"gq_matmul_ex({self.name}) failed: {gq.strerror(rc)}")
 
 
 def capture(fn):
-    """Capture fn(stream_ptr) into a torch CUDA (HIP) graph."""
+    """Capture fn(stream_ptr) into a HIP graph (torch.cuda.CUDAGraph)."""
     import torch
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        fn(ctypes.c_void_p(s.cuda_stream))          # warm (outside capture)
+        fn(ctypes.c_void_p(s.cuda_stream))          # warm, outside capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     with torch.cuda.graph(g):
@@ -116,36 +151,52 @@ def time_graphs(graphs, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def kernel_time_ms(mat, steps, launches_per_graph=16, n=1, x=None, y=None):
-    """Live HIP-event timing of back-to-back launches of one kernel, rotating
-    over copies of its blob totalling >= 2x the Infinity Cache."""
-    need = max(2, -(-2 * CACHE_BYTES // mat.bytes))
-    while len(mat.copies) < need:
-        mat.copies.append(mat.copies[0].clone())
-    ng = -(-len(mat.copies) // launches_per_graph)
+def kernel_time_ms(mat, steps, per_graph=16):
+    """Live HIP-event timing of back-to-back launches of one matrix, rotating
+    over copies totalling >= 2x the Infinity Cache."""
+    mat.ensure_copies(2 * CACHE_BYTES)
     graphs = []
-    for gi in range(ng):
+    for gi in range(-(-len(mat.copies) // per_graph)):
         def fn(sp, gi=gi):
-            for j in range(launches_per_graph):
-                mat.launch(gi * launches_per_graph + j, sp, n=n, x=x, y=y)
+            for j in range(per_graph):
+                mat.launch(gi * per_graph + j, sp)
         graphs.append(capture(fn))
-    reps = max(4, steps // launches_per_graph)
-    ms = time_graphs(graphs, reps, warmup=2)
-    return ms / launches_per_graph
+    ms = time_graphs(graphs, max(4, steps // per_graph), warmup=2)
+    return ms / per_graph
 
 
-def cpu_baseline(mats, xs):
+def traffic_from_profile(kernel_bytes):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when absent or taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"k_gemv\.hip sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_k = re.search(r"for_blob_bytes:\s*(\d+)", text)
+    if not (m_sha and m_b and m_k) or int(m_k.group(1)) != kernel_bytes:
+        return None
+    if hashlib.sha256(open(GEMV_SRC, "rb").read()).hexdigest() != m_sha.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(layer_mats):
     import numpy as np
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    blobs = [oracle.quantize(m.w, m.t) for m in mats]       # the oracle's own blobs
-    total = sum(b.size for b in blobs)
+    work = []
+    for m in layer_mats:
+        blob = np.concatenate([oracle.quantize(w, m.t) for w in m.w])   # the oracle's own blobs
+        work.append((m, blob, m.x_host))
+    total = sum(b.size for _, b, _ in work)
     res = {}
     for th in (1, threads):
         ts = []
         for _ in range(3 if th > 1 else 1):
             t0 = time.perf_counter()
-            for m, b, x in zip(mats, blobs, xs):
+            for m, b, x in work:
                 oracle.matmul_f64(b, m.t, m.rows, m.cols, x, threads=th)
             ts.append(time.perf_counter() - t0)
         res[th] = float(np.median(ts))
@@ -161,31 +212,77 @@ def cpu_baseline(mats, xs):
     return {
         "value": round(total / res[threads] / 1e9, 3), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
-        "sample": f"the full layer once per repetition (7 matrices, {total} blob bytes), "
-                  f"fp64 dequant-then-dot, median of 3; 1-thread: "
+        "sample": f"the whole layer (4 matrices, {total} blob bytes) per repetition, fp64 "
+                  f"dequant-then-dot, median of 3 on {threads} threads; 1 thread: "
                   f"{round(total / res[1] / 1e9, 3)} GB/s ({res[1]:.2f} s); CPU: {cpu}",
     }
+
+
+def sweep(steps):
+    """Secondary shapes: one line each, graph-timed with rotating copies."""
+    import synth
+    out = []
+    cases = [("single q4_k 2048x2048", "q4_k", [("w", 2048)], 2048, 1, "f32")]
+    cases += [(f"per-type {t} {r}x{c}", t, [(n, r)], c, 1, "f32") for n, t, r, c in synth.PER_TYPE_SWEEP_4096]
+    cases += [(f"q4_k 11008x4096 n={n} f16", "q4_k", [("w", 11008)], 4096, n, "f16") for n in synth.GEMM_TOKENS]
+    for n in synth.LLAMA3_8B_TOKENS:
+        for name, t, r, c in synth.LLAMA3_8B_LAYER_Q4KM:
+            cases.append((f"llama3-8b {name} {t} {r}x{c} n={n}", t, [(name, r)], c, n, "f32" if n == 1 else "f16"))
+    for i, (label, t, parts, cols, n, xdt) in enumerate(cases):
+        m = Mat(label, t, parts, cols, seed=9000 + 31 * i, ncopies=1, n_tok=n, x_dtype=xdt)
+        ms = kernel_time_ms(m, max(64, steps // 2), per_graph=8 if m.bytes > (64 << 20) else 16)
+        flops = 2.0 * m.rows * cols * n
+        out.append({"case": label, "blob_bytes": m.bytes, "us": round(ms * 1e3, 2),
+                    "GBps": round(m.bytes / (ms * 1e-3) / 1e9, 1),
+                    "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)})
+        log(f"  {label}: {ms*1e3:.2f} us  {out[-1]['GBps']} GB/s  {out[-1]['TFLOPs']} TFLOP/s")
+        del m
+    return out
+
+
+def profile_launches(mats, n):
+    """Plain launches for rocprofv3, in dispatch order: each layer matrix n
+    times in turn (rotating copies), then n single-dispatch elementwise
+    copies that read 256 MiB and write 256 MiB (counter calibration)."""
+    import torch
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for m in mats:
+        m.ensure_copies(2 * CACHE_BYTES)
+    torch.cuda.synchronize()
+    for m in mats:
+        for i in range(n):
+            m.launch(i, sp)
+        torch.cuda.synchronize()
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(n):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"profile: {n} launches each of {[m.name for m in mats]}, then {n} elementwise copies "
+        f"of {src.numel() * 4} bytes")
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
     import gguf_quant_matmul_amd as gq
-    import synth
 
     gq.lib()
     torch.cuda.init()
-    layer = synth.LLAMA7B_LAYER_Q4KM
-    layer_bytes = sum(gq.row_bytes(t, c) * r for _, t, r, c in layer)
+    layer_bytes = sum(gq.row_bytes(t, c) * sum(r for _, r in parts) for _, t, parts, c in LAYER)
     ncopy = max(2, -(-(2 * CACHE_BYTES + CACHE_BYTES // 2) // layer_bytes))
-    log(f"setup: {len(layer)} matrices, {layer_bytes} blob bytes, {ncopy} rotating copies")
-    mats = [Mat(n, t, r, c, seed=7000 + 17 * i, ncopies=ncopy) for i, (n, t, r, c) in enumerate(layer)]
+    log(f"setup: {len(LAYER)} launches per step, {layer_bytes} blob bytes, {ncopy} rotating copies")
+    mats = [Mat(n, t, parts, c, seed=7000 + 17 * i, ncopies=ncopy, keep_w=not args.no_cpu)
+            for i, (n, t, parts, c) in enumerate(LAYER)]
     torch.cuda.synchronize()
+
+    if args.profile_launches:
+        profile_launches(mats, args.profile_launches)
+        return
 
     step_graphs = []
     for ci in range(ncopy):
@@ -197,51 +294,45 @@ def main():
     ms = time_graphs(step_graphs, args.steps, args.warmup)
     value = layer_bytes / (ms * 1e-3) / 1e9
 
-    # per-kernel live timing; kernels are distinct per (type, launch shape)
-    per = []
+    # per-kernel live timing; a kernel is a (type, launch shape) instantiation
+    per, kernels = [], {}
     for m in mats:
         kms = kernel_time_ms(m, args.steps)
-        per.append({"matrix": m.name, "type": m.t, "rows": m.rows, "cols": m.cols,
+        per.append({"launch": m.name, "type": m.t, "rows": m.rows, "cols": m.cols,
                     "blob_bytes": m.bytes, "us_per_launch": round(kms * 1e3, 3),
                     "GBps": round(m.bytes / (kms * 1e-3) / 1e9, 1)})
-        log(f"  {m.name:9s} {m.t} {m.rows}x{m.cols}: {kms*1e3:.2f} us  {per[-1]['GBps']} GB/s")
-    # group identical launch shapes (same kernel instantiation)
-    groups = {}
-    for p in per:
-        k = (p["type"], p["rows"], p["cols"])
-        g = groups.setdefault(k, {"launches": 0, "us": p["us_per_launch"], "bytes": p["blob_bytes"]})
-        g["launches"] += 1
-    dom_key = max(groups, key=lambda k: groups[k]["launches"] * groups[k]["us"])
-    dom = groups[dom_key]
-    achieved = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+        log(f"  {m.name:12s} {m.t} {m.rows}x{m.cols}: {kms*1e3:.2f} us  {per[-1]['GBps']} GB/s")
+        key = f"gemv {m.t}, {m.cols} cols, fp32 x, batch 1"
+        k = kernels.setdefault(key, {"launches": 0, "us": 0.0, "bytes": 0})
+        k["launches"] += 1
+        k["us"] += kms * 1e3
+        k["bytes"] += m.bytes
+    dom_key = max(kernels, key=lambda k: kernels[k]["us"])
+    dom = kernels[dom_key]
+    avg_us = dom["us"] / dom["launches"]
+    avg_bytes = dom["bytes"] / dom["launches"]
+    achieved = avg_bytes / (avg_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(int(avg_bytes))
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": f"gemv {dom_key[0]} {dom_key[1]}x{dom_key[2]} batch 1 fp32 x",
-                "per_launch_bytes": dom["bytes"], "us_per_launch": dom["us"]}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": dom_key, "launches_per_step": dom["launches"],
+                "bytes_per_launch": avg_bytes, "us_per_launch": round(avg_us, 3)}
 
-    secondary = None
-    if not args.no_gemm:
-        name, t, r, c = synth.GEMM_Q4K_11008[0]
-        gm = Mat(name, t, r, c, seed=9000, ncopies=1)
-        n = 512
-        xg = torch.from_numpy(synth.activations(n, c, seed=9001, dtype="f16")).cuda()
-        yg = torch.empty((n, r), dtype=torch.float32, device="cuda")
-        gms = kernel_time_ms(gm, max(64, args.steps // 2), launches_per_graph=8, n=n, x=xg, y=yg)
-        flops = 2.0 * r * c * n
-        tf = flops / (gms * 1e-3) / 1e12
+    secondary, shapes = None, None
+    if not args.no_sweep:
+        shapes = sweep(args.steps)
+        g = [s for s in shapes if s["case"] == "q4_k 11008x4096 n=512 f16"][0]
+        tf = g["TFLOPs"]
         secondary = {"metric": "Q4_K 11008x4096 dequant-GEMM GFLOP/s at 512 fp16 tokens",
-                     "value": round(tf * 1e3, 1), "unit": "GFLOP/s", "us_per_launch": round(gms * 1e3, 2),
-                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP16_PEAK_TFLOPS,
+                     "value": round(tf * 1e3, 1), "unit": "GFLOP/s", "us_per_launch": g["us"],
+                     "roofline": {"bound": "mfma", "achieved": tf, "peak": FP16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TFLOPS, 4),
                                   "traffic": None}}
-        log(f"  gemm n=512: {gms*1e3:.1f} us  {tf:.1f} TFLOP/s")
-        del gm
 
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        xs = [m.x.cpu().numpy() for m in mats]
-        cpu = cpu_baseline(mats, xs)
+        cpu = cpu_baseline(mats)
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -249,13 +340,14 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded N(0,0.02) weights quantized on the GPU, N(0,1) activations)",
         "config": {"workload": "Llama-7B-shaped decode layer, Q4_K_M mix, batch 1",
-                   "matrices": [f"{n} {t} {r}x{c}" for n, t, r, c in layer],
+                   "launches": [f"{n} {t} {sum(r for _, r in p)}x{c}" for n, t, p, c in LAYER],
                    "layer_blob_bytes": layer_bytes, "n_tok": 1, "x_dtype": "f32",
                    "rotating_copies": ncopy, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
-        "per_matrix": per,
+        "per_launch": per,
+        "sweep": shapes,
     }
     print(json.dumps(out), flush=True)
 
