@@ -12,7 +12,9 @@ namespace {
 constexpr int64_t kDim = (int64_t)1 << 31;       // rows, cols, n_tok < 2^31
 constexpr int64_t kBytes = (int64_t)1 << 47;     // any one buffer < 2^47 bytes
 constexpr int64_t kMaxColsGemv = 16384;          // x staged in 64 KB of LDS
+constexpr int64_t kMaxColsBatch = (int64_t)1 << 24;  // n_tok >= 2: 16 tokens of x in 32-bit offsets
 constexpr int64_t kMaxTokens = (int64_t)1 << 22;  // matrix-core grid.y = n_tok / 64 < 65536
+constexpr int64_t kSmallBatch = 64;               // n_tok up to this: weight-stream kernel
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // dequant / quantize grid.x < 2^31
 
 bool quant_type(int t) { return t >= GQ_Q4_0 && t <= GQ_Q6_K; }
@@ -90,6 +92,7 @@ int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t c
   if (n_tok >= kDim) return GQ_EOVERFLOW;
   if (n_tok == 0) return GQ_OK;
   if (n_tok == 1 && cols > kMaxColsGemv) return GQ_EOVERFLOW;
+  if (n_tok >= 2 && cols > kMaxColsBatch) return GQ_EOVERFLOW;
   if (n_tok > kMaxTokens) return GQ_EOVERFLOW;
   if (n_tok > kBytes / cols || n_tok > kBytes / rows) return GQ_EOVERFLOW;
   if (!weight_blob || !x || !y) return GQ_EINVAL_PTR;
@@ -102,6 +105,8 @@ int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t c
   hipStream_t st = (hipStream_t)stream;
   const bool xf16 = (x_type == GQ_F16);
   if (n_tok == 1) return hip_status(gq::launch_gemv(ggml_type, weight_blob, rows, cols, x, xf16, y, st));
+  if (n_tok <= kSmallBatch)
+    return hip_status(gq::launch_mmv(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
   return hip_status(gq::launch_mfma(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
 }
 

@@ -42,6 +42,30 @@ __device__ __forceinline__ uint32_t ld2u(const uint8_t* p) {
   return *reinterpret_cast<const u16u*>(p);
 }
 
+// Raw buffer loads through a scalar resource: byte offsets are 32-bit and
+// any load whose offset reaches past the resource's size returns zero without
+// touching memory (the range check covers the vector offset plus the
+// instruction offset).
+constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer resource word 3 (gfx950)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, kRsrcWord3);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + imm, 0, 0));
+}
+__device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff + imm, 0, 0));
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff + imm, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff + imm, 0, 0);
+}
+// A vector offset no resource reaches (resources here stay below 2^31 bytes).
+constexpr int kOobOff = 0x7FFF0000;
+
 // fp16 bit pattern (low 16 bits of h) -> fp32, exact (subnormals included).
 __device__ __forceinline__ float h2f(uint32_t h) {
   _Float16 v = __builtin_bit_cast(_Float16, (uint16_t)(h & 0xFFFFu));

@@ -13,7 +13,11 @@ hipError_t launch_quantize(int type, const float* w, int64_t rows, int64_t cols,
 // One token (n_tok == 1): the bandwidth-bound GEMV family.
 hipError_t launch_gemv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, hipStream_t st);
-// n_tok >= 2: weights decoded once, reused for every token on the matrix cores.
+// Small batches: the weight stream on the matrix cores, 16 tokens per pass.
+hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
+                      bool x_f16, float* y, int64_t n_tok, hipStream_t st);
+// Larger batches: weights decoded once per 16..128-token pass, reused for
+// every token on the matrix cores.
 hipError_t launch_mfma(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, int64_t n_tok, hipStream_t st);
 

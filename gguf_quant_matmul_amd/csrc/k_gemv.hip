@@ -23,21 +23,6 @@
 
 namespace gq {
 
-constexpr int kRsrcWord3 = 0x00020000;   // raw 32-bit buffer resource word 3 (gfx950)
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, kRsrcWord3);
-}
-__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + imm, 0, 0));
-}
-__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff + imm, 0, 0);
-}
-__device__ __forceinline__ uint32_t bld2(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, voff + imm, 0, 0);
-}
-
 // acc + sum over the 4 bytes of w of (byte as unsigned / signed) * x[k]
 __device__ __forceinline__ float dot4u(uint32_t w, const float* x, float acc) {
   acc = fmaf(ub0(w), x[0], acc);

@@ -1,0 +1,449 @@
+// k_mmv.hip — small-batch matmul over GGUF blocks (2 <= n_tok, a few token
+// passes of 16) on the gfx950 matrix cores.  Each weight is decoded once per
+// 16-token pass and reused for every token of the pass ("Local LLM
+// inference", "The mmap backend"); with so few tokens the work is still
+// bound by the weight stream ("12 — llama.cpp / GGUF", "The bandwidth cap"),
+// so the kernel is built around keeping enough weight bytes in flight:
+//
+//   * a workgroup owns one tile of 16 weight rows; its KS waves split the
+//     row's 256-weight slabs (slab s goes to wave s % KS), so even a
+//     4096-row matrix spreads over every compute unit;
+//   * every wave streams its slabs through a D-deep register ring that holds
+//     both the weights and the matching activations: loads complete in issue
+//     order, so activations fetched later than the weights would cap the
+//     weights' prefetch distance at their own;
+//   * activations are fetched with whole-cache-line loads (each load
+//     instruction covers 8 full 128-byte lines) and moved into the matrix
+//     op's A layout through the wave's own block of LDS.  Loading them
+//     directly in A layout would touch 64 lines per instruction, and the
+//     per-CU load pipeline, not HBM, would then set the speed;
+//   * the contraction is v_mfma_f32_16x16x32_f16 with A = 16 tokens x 32 k of
+//     x and B = 32 k x 16 rows of decoded weights.  Each lane's 8 k values
+//     are 8 consecutive columns; the weight bytes are put into that order
+//     with v_perm_b32, which also ORs in the fp16 exponent;
+//   * B holds exact integers wherever the format allows (Hitchhiker's Guide
+//     §11.2, w = (d*sc)*q - dmin*m): Q4_K B = sc*q (<= 945) with the min
+//     term as a second product of x with m (<= 63), both scaled by the
+//     block's d and dmin in fp32; Q6_K B = RNE_fp16(sc*(q-32)) (exact unless
+//     |sc*(q-32)| > 2048); Q4_0 / Q5_0 / Q8_0 B = q - offset with d applied
+//     per block in fp32.  fp32 x is split into two fp16 parts (hi, lo) that
+//     both go through the matrix op;
+//   * the KS partial tiles are summed in LDS in wave order, so the result is
+//     the same on every run.
+#include "gq_device.h"
+#include "gq_launch.h"
+
+namespace gq {
+
+namespace {
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f16x2 as_h2(uint32_t v) { return __builtin_bit_cast(f16x2, v); }
+__device__ __forceinline__ uint32_t as_u(f16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+__device__ __forceinline__ f16x2 hpair(float a, float b) { return f16x2{(_Float16)a, (_Float16)b}; }
+__device__ __forceinline__ f16x8 cat8(f16x2 a, f16x2 b, f16x2 c, f16x2 d) {
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Bytes 0,1 (PAIR 0) or 2,3 (PAIR 1) of v as the low bytes of two fp16
+// values whose high byte is E (v_perm_b32; selector 4 picks byte 0 of E).
+template <int PAIR>
+__device__ __forceinline__ f16x2 bytes_as_h2(uint32_t e4, uint32_t v) {
+  return as_h2(__builtin_amdgcn_perm(e4, v, PAIR ? 0x04030402u : 0x04010400u));
+}
+// Eight bytes (two dwords) -> eight fp16 values with high byte E, in byte order.
+__device__ __forceinline__ void bytes8(uint32_t e4, uint32_t v0, uint32_t v1, f16x2 o[4]) {
+  o[0] = bytes_as_h2<0>(e4, v0);
+  o[1] = bytes_as_h2<1>(e4, v0);
+  o[2] = bytes_as_h2<0>(e4, v1);
+  o[3] = bytes_as_h2<1>(e4, v1);
+}
+constexpr uint32_t kE1024 = 0x64646464u;   // fp16 0x64XX = 1024 + XX
+constexpr uint32_t kE256 = 0x5C5C5C5Cu;    // fp16 0x5CXX = 256 + XX / 4
+
+// ---------------------------------------------------------------------------
+// Activation slot: one slab (256 columns) of the pass's P tokens as loaded.
+// fp16: load i, lane l holds token 2i + l/32, 16-byte chunk l%32 (8 columns).
+// fp32: load i, lane l holds token i, columns 4l .. 4l+3.
+template <bool XLO, int P> struct XS {
+  u32x4 v[XLO ? P : P / 2];
+};
+
+// The wave's LDS block: token t's 256 columns at t * 512 bytes, 16-byte chunk
+// k stored at position k ^ (t & 7), so the 8 lanes that LDS serves together
+// hit 8 different bank groups both when storing a load's chunks and when
+// reading A fragments.  fp32 activations store hi = RNE_fp16(x) in the first
+// P rows and lo = RNE_fp16(x - hi) in the next P.
+__device__ __forceinline__ int xslot(int t, int k) { return t * 512 + ((k ^ (t & 7)) << 4); }
+
+template <bool XLO, int P>
+__device__ __forceinline__ void stage_x(uint8_t* xw, const XS<XLO, P>& xs, int lane) {
+  if constexpr (!XLO) {
+#pragma unroll
+    for (int i = 0; i < P / 2; i++)
+      *reinterpret_cast<u32x4*>(xw + xslot(2 * i + (lane >> 5), lane & 31)) = xs.v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      const f32x4 f = __builtin_bit_cast(f32x4, xs.v[i]);
+      f16x2 h[2], l[2];
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        const _Float16 a = (_Float16)f[2 * e], b = (_Float16)f[2 * e + 1];
+        h[e] = f16x2{a, b};
+        l[e] = f16x2{(_Float16)(f[2 * e] - (float)a), (_Float16)(f[2 * e + 1] - (float)b)};
+      }
+      const int o = xslot(i, lane >> 1) + 8 * (lane & 1);
+      *reinterpret_cast<u32x2*>(xw + o) = u32x2{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1])};
+      *reinterpret_cast<u32x2*>(xw + P * 512 + o) =
+          u32x2{__builtin_bit_cast(uint32_t, l[0]), __builtin_bit_cast(uint32_t, l[1])};
+    }
+  }
+}
+
+// A fragment (8 consecutive columns, chunk k of the slab) of token row t.
+// With P = 8 the upper 8 MFMA rows repeat rows 0..7; their results are not stored.
+template <int P>
+__device__ __forceinline__ f16x8 read_a(const uint8_t* xw, int t, int k) {
+  const int tt = (P == 8) ? (t & 7) : t;
+  return *reinterpret_cast<const f16x8*>(xw + xslot(tt, k));
+}
+
+// ---------------------------------------------------------------------------
+// Weight slot: the lane's share of one slab of its row.
+template <int T> struct WS;
+
+template <> struct WS<GQ_Q4_K> {     // slab = one super-block; sub-blocks 2g, 2g+1
+  u32x4 hd, q[2];
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int g) {
+    hd = bld16(r, vo, 0);
+    q[0] = bld16(r, vo + 32 * g, 16);
+    q[1] = bld16(r, vo + 32 * g, 32);
+  }
+};
+
+template <> struct WS<GQ_Q6_K> {     // slab = one super-block; 32-groups 2g, 2g+1
+  u32x4 l[2], h;
+  uint32_t sc4, d;
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int g) {
+    l[0] = bld16(r, vo + 32 * g, 18);
+    l[1] = bld16(r, vo + 32 * g, 34);
+    h = bld16(r, vo + 16 * g, 146);
+    sc4 = bld4(r, vo + 4 * g, 2);
+    d = bld2(r, vo, 0);
+  }
+};
+
+// 32-weight types: slab = 8 blocks; chunk j = the lane's 8 weights of block j.
+// vd[j] is block j's offset, or an out-of-range offset when the block lies
+// past the row's end (then d reads as 0 and the block adds nothing).
+template <int T> struct WS32 {
+  static constexpr int BB = Geo<T>::BB;
+  u32x2 c[8];
+  uint32_t d[8], qh[8];
+  __device__ void load(__amdgpu_buffer_rsrc_t r, const int* vd, int vc, int g) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      d[j] = bld2(r, vd[j], j * BB);
+      if constexpr (T == GQ_Q8_0) c[j] = bld8(r, vc + 8 * g, j * BB + 2);
+      if constexpr (T == GQ_Q4_0) c[j] = bld8(r, vc + 8 * (g & 1), j * BB + 2);
+      if constexpr (T == GQ_Q5_0) {
+        c[j] = bld8(r, vc + 8 * (g & 1), j * BB + 6);
+        qh[j] = bld4(r, vc, j * BB + 2);
+      }
+    }
+  }
+};
+template <> struct WS<GQ_Q4_0> : WS32<GQ_Q4_0> {};
+template <> struct WS<GQ_Q5_0> : WS32<GQ_Q5_0> {};
+template <> struct WS<GQ_Q8_0> : WS32<GQ_Q8_0> {};
+
+// Bit b (b = 0..3) of v4 to bit 4 of byte b: the multiply places bit b at
+// bits b + 7k (k = 0..3), all distinct, so no carries; bit 8b is the k = b copy.
+__device__ __forceinline__ uint32_t bits_to_b4(uint32_t v4) {
+  return (((v4 & 0xFu) * 0x00204081u) & 0x01010101u) << 4;   // a 24-bit multiply
+}
+
+// P += A(chunk k) x B, with fp32 activations as hi + lo.
+template <bool XLO, int P>
+__device__ __forceinline__ void mma(const uint8_t* xw, int t, int k, f16x8 B, f32x4v& Pc) {
+  Pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a<P>(xw, t, k), B, Pc, 0, 0, 0);
+  if constexpr (XLO) Pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a<P>(xw + P * 512, t, k), B, Pc, 0, 0, 0);
+}
+
+// acc += the slab's contribution for this wave's 16 rows x 16 tokens.
+// Activation chunk of MFMA step j for lane group g: K-quant lanes own columns
+// 64 g .. 64 g + 63 (their two sub-blocks), 32-weight types 32 j + 8 g.
+template <int T, bool XLO, int P>
+__device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& ws, int g, f32x4v& acc) {
+  const f32x4v z = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (T == GQ_Q4_K) {
+    const float d = h2f(ws.hd.x), dmin = h2f(ws.hd.x >> 16);
+    f16x8 M[2];
+    f16x2 SL[2], NL[2], SH[2], NH[2];
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const uint32_t f = q4k_pair(ws.hd.y, ws.hd.z, ws.hd.w, 2 * g + h);
+      const float sc = (float)(f & 63u), m = (float)(f >> 6);
+      SL[h] = hpair(sc, sc);                  // low nibble q: (1024 + q) * sc - 1024 sc
+      NL[h] = hpair(-1024.f * sc, -1024.f * sc);
+      SH[h] = hpair(sc * 0.0625f, sc * 0.0625f);   // high nibble: (1024 + 16 q) * sc/16 - 64 sc
+      NH[h] = hpair(-64.f * sc, -64.f * sc);
+      const _Float16 mh = (_Float16)m;
+      M[h] = f16x8{mh, mh, mh, mh, mh, mh, mh, mh};
+    }
+    f32x4v Pk = z, Pm = z;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int h = j >> 2, qq = j & 3;       // sub-block 2g + h, eighth qq
+      const uint32_t D0 = ws.q[h][2 * (qq & 1)], D1 = ws.q[h][2 * (qq & 1) + 1];
+      const uint32_t msk = (qq < 2) ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+      f16x2 v[4];
+      bytes8(kE1024, D0 & msk, D1 & msk, v);
+      const f16x2 s = (qq < 2) ? SL[h] : SH[h], n = (qq < 2) ? NL[h] : NH[h];
+      const f16x8 B = cat8(__builtin_elementwise_fma(v[0], s, n), __builtin_elementwise_fma(v[1], s, n),
+                           __builtin_elementwise_fma(v[2], s, n), __builtin_elementwise_fma(v[3], s, n));
+      const f16x8 ah = read_a<P>(xw, t, 8 * g + j);
+      Pk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, B, Pk, 0, 0, 0);
+      Pm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, M[h], Pm, 0, 0, 0);
+      if constexpr (XLO) {
+        const f16x8 al = read_a<P>(xw + P * 512, t, 8 * g + j);
+        Pk = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, B, Pk, 0, 0, 0);
+        Pm = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, M[h], Pm, 0, 0, 0);
+      }
+    }
+    acc += d * Pk;
+    acc -= dmin * Pm;
+  } else if constexpr (T == GQ_Q6_K) {
+    const float d = h2f(ws.d);
+    f32x4v Pk = z;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int h = j >> 2, qq = j & 3;       // 32-group 2g + h, eighth qq
+      const uint32_t L0 = ws.l[h][2 * (qq & 1)], L1 = ws.l[h][2 * (qq & 1) + 1];
+      const uint32_t H0 = ws.h[2 * h], H1 = ws.h[2 * h + 1];
+      // 4 * q per byte: low 4 bits from the ql nibble, top 2 from qh bits 2qq..2qq+1
+      const uint32_t c0 = ((qq < 2 ? L0 << 2 : L0 >> 2) & 0x3C3C3C3Cu) | ((H0 << (6 - 2 * qq)) & 0xC0C0C0C0u);
+      const uint32_t c1 = ((qq < 2 ? L1 << 2 : L1 >> 2) & 0x3C3C3C3Cu) | ((H1 << (6 - 2 * qq)) & 0xC0C0C0C0u);
+      f16x2 v[4];
+      bytes8(kE256, c0, c1, v);               // 256 + q
+      const float sc = (float)(int)(int8_t)(ws.sc4 >> (8 * (2 * h + (qq >> 1))));
+      const f16x2 s = hpair(sc, sc), n = hpair(-288.f * sc, -288.f * sc);
+      const f16x8 B = cat8(__builtin_elementwise_fma(v[0], s, n), __builtin_elementwise_fma(v[1], s, n),
+                           __builtin_elementwise_fma(v[2], s, n), __builtin_elementwise_fma(v[3], s, n));
+      mma<XLO, P>(xw, t, 8 * g + j, B, Pk);
+    }
+    acc += d * Pk;
+  } else {
+    const f16x2 off = (T == GQ_Q8_0) ? hpair(-1152.f, -1152.f)
+                      : (T == GQ_Q5_0) ? hpair(-1040.f, -1040.f) : hpair(-1032.f, -1032.f);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      uint32_t c0 = ws.c[j][0], c1 = ws.c[j][1];
+      if constexpr (T == GQ_Q8_0) {
+        c0 ^= 0x80808080u;                    // signed byte + 128
+        c1 ^= 0x80808080u;
+      } else {
+        const int sh = 4 * (g >> 1);          // low nibbles for g < 2, high for g >= 2
+        c0 = (c0 >> sh) & 0x0F0F0F0Fu;
+        c1 = (c1 >> sh) & 0x0F0F0F0Fu;
+        if constexpr (T == GQ_Q5_0) {
+          const uint32_t hb = ws.qh[j] >> (8 * g);   // fifth bits of elements 8g .. 8g+7
+          c0 |= bits_to_b4(hb);
+          c1 |= bits_to_b4(hb >> 4);
+        }
+      }
+      f16x2 v[4];
+      bytes8(kE1024, c0, c1, v);
+      const f16x8 B = cat8(v[0] + off, v[1] + off, v[2] + off, v[3] + off);
+      f32x4v Pk = z;
+      mma<XLO, P>(xw, t, 4 * j + g, B, Pk);
+      acc += h2f(ws.d[j]) * Pk;
+    }
+  }
+}
+
+}  // namespace
+
+// grid: tiles * passes workgroups of 64 * KS threads, P tokens per pass,
+// KS * P * 512 bytes of LDS (twice that for fp32 activations).  With several
+// token passes the workgroup index is remapped so that the passes of one row
+// tile run back to back on one XCD (workgroups go round-robin over the 8
+// XCDs), where the tile's weights are still in that XCD's L2.
+template <int T, bool XLO, int P, int D>
+__global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, int rows, int cols,
+                                             int rb, const void* __restrict__ xv, int n,
+                                             float* __restrict__ y, int tiles, int passes) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr bool KQ = (T == GQ_Q4_K || T == GQ_Q6_K);
+  constexpr int ES = XLO ? 4 : 2;
+  constexpr int XB = P * 512 * (XLO ? 2 : 1);   // LDS bytes per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int KS = blockDim.x >> 6;
+  int tile = blockIdx.x, pass = 0;
+  if (passes > 1) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    tile = (slot / passes) * 8 + xcd;
+    pass = slot % passes;
+    if (tile >= tiles) return;                // whole workgroup: uniform
+  }
+  const int row0 = tile * 16, tok0 = pass * P;
+  const int r = lane & 15, g = lane >> 4;
+  const int nr = min(16, rows - row0), nt = min(P, n - tok0);
+  const __amdgpu_buffer_rsrc_t WR = make_rsrc(blob + (int64_t)row0 * rb, (uint32_t)(nr * rb));
+  const __amdgpu_buffer_rsrc_t XR =
+      make_rsrc((const uint8_t*)xv + (int64_t)tok0 * cols * ES, (uint32_t)(nt * cols * ES));
+  const int nslab = (cols + 255) >> 8;
+  const int nblk = cols >> 5;
+  const int wl = r * rb;                      // lane's row within the tile
+  uint8_t* const xw = lds + w * XB;           // this wave's activation block
+
+  auto load = [&](XS<XLO, P>& xs, WS<T>& ws, int s) {
+    if constexpr (KQ) {
+      ws.load(WR, s < nslab ? wl + s * Geo<T>::BB : kOobOff, g);
+    } else {
+      const int b0 = s * 8;
+      const int vc = wl + b0 * Geo<T>::BB;    // codes: past-the-end blocks read finite bytes
+      int vd[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) vd[j] = (b0 + j < nblk) ? vc : kOobOff;
+      ws.load(WR, vd, vc, g);
+    }
+    // activations: whole lines; columns past the row (or past the last
+    // block) and tokens past the pass read as zero
+    const int c = s * 256 + (XLO ? 4 * lane : 8 * (lane & 31));
+    const bool ok = KQ ? (s < nslab) : ((c >> 5) < nblk);
+#pragma unroll
+    for (int i = 0; i < (XLO ? P : P / 2); i++) {
+      const int tok = XLO ? i : 2 * i + (lane >> 5);
+      xs.v[i] = bld16(XR, ok ? (tok * cols + c) * ES : kOobOff, 0);
+    }
+  };
+
+  const int cnt = (nslab - 1 - w) / KS + 1;   // this wave's slabs (w < KS <= nslab)
+  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  XS<XLO, P> xs[D];
+  WS<T> ws[D];
+#pragma unroll
+  for (int i = 0; i < D; i++) {
+    load(xs[i], ws[i], w + i * KS);           // issued in ring order (see below)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Every wave has at least one slab (KS <= slabs per row), so the loop is a
+  // do-while: with a guarded loop the compiler sinks the first loads into
+  // the guard in another order, and the waits in the loop follow the
+  // stricter of the two orders.
+  int m0 = 0;
+  do {
+#pragma unroll
+    for (int i = 0; i < D; i++) {
+      // The barriers keep the scheduler from sinking the reloads to the end
+      // of the unrolled body, which would make every step wait on them all.
+      // LDS operations of one wave run in order, so the block can be
+      // rewritten while the previous slab's reads are still queued.
+      stage_x<XLO, P>(xw, xs[i], lane);
+      slab_mma<T, XLO, P>(xw, r, ws[i], g, acc);   // slabs past cnt read as zeros
+      __builtin_amdgcn_sched_barrier(0);
+      load(xs[i], ws[i], w + (m0 + i + D) * KS);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    m0 += D;
+  } while (m0 < cnt);
+
+  // D lane l holds rows (tokens) 4(l/16) + v of column (weight row) l % 16
+  if (KS == 1) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int t = 4 * g + v;
+      if (t < nt && r < nr) y[(int64_t)(tok0 + t) * rows + row0 + r] = acc[v];
+    }
+    return;
+  }
+  __syncthreads();                            // every wave is done with its block
+  f32x4v* red = reinterpret_cast<f32x4v*>(lds);   // [KS][64]
+  red[w * 64 + lane] = acc;
+  __syncthreads();
+  for (int o = threadIdx.x; o < 256; o += blockDim.x) {
+    const int t = o >> 4, rr = o & 15;
+    const int src = 16 * (t >> 2) + rr, v = t & 3;
+    float sum = 0.f;
+    for (int k = 0; k < KS; k++) sum += red[k * 64 + src][v];
+    if (t < nt && rr < nr) y[(int64_t)(tok0 + t) * rows + row0 + rr] = sum;
+  }
+}
+
+namespace {
+
+template <int T, bool XLO, int P, int D>
+hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n,
+                      float* y, int ks, hipStream_t st) {
+  const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
+  const int64_t es = XLO ? 4 : 2;
+  // every resource and offset must stay below the out-of-range marker
+  if (16 * rb >= kOobOff || (int64_t)P * cols * es >= kOobOff) return hipErrorInvalidValue;
+  const int64_t tiles = (rows + 15) / 16, passes = (n + P - 1) / P;
+  const int64_t grid = passes == 1 ? tiles : (tiles + 7) / 8 * 8 * passes;
+  const size_t lds = (size_t)ks * P * 512 * (XLO ? 2 : 1);
+  hipLaunchKernelGGL((k_mmv<T, XLO, P, D>), dim3((unsigned)grid), dim3(64 * ks), lds, st,
+                     (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tiles,
+                     (int)passes);
+  return hipGetLastError();
+}
+
+#ifndef GQ_MMV_WAVES
+#define GQ_MMV_WAVES 4096                     // target waves per launch
+#endif
+#ifndef GQ_MMV_DEPTH
+#define GQ_MMV_DEPTH 2                        // ring depth with fp16 activations
+#endif
+
+// KS: enough waves to cover the chip GQ_MMV_WAVES / 256 deep, at most 8 per
+// workgroup (and as many as 64 KB of LDS hold), and no more than the row has
+// slabs.
+int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave) {
+  const int64_t tiles = (rows + 15) / 16, passes = (n + p - 1) / p;
+  const int64_t nslab = (cols + 255) / 256;
+  int ks = 1;
+  while (ks < 8 && (ks * 2) * lds_per_wave <= 65536 && tiles * passes * ks * 2 <= GQ_MMV_WAVES &&
+         ks * 2 <= nslab)
+    ks *= 2;
+  return ks;
+}
+
+template <int T, bool XLO, int P>
+hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
+                 hipStream_t st) {
+  // ring depth: as deep as the registers allow without spilling
+  constexpr int D = XLO ? (P == 8 ? 2 : 1) : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
+  return mmv_launch<T, XLO, P, D>(blob, rows, cols, x, n, y,
+                                  pick_ks(rows, cols, n, P, P * 512 * (XLO ? 2 : 1)), st);
+}
+
+template <int T, bool XLO>
+hipError_t mmv_t(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
+                 hipStream_t st) {
+  return n <= 8 ? mmv_p<T, XLO, 8>(blob, rows, cols, x, n, y, st)
+                : mmv_p<T, XLO, 16>(blob, rows, cols, x, n, y, st);
+}
+
+}  // namespace
+
+hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
+                      bool x_f16, float* y, int64_t n_tok, hipStream_t st) {
+  switch (type) {
+#define GQ_MMV_CASE(TT)                                                                   \
+  case TT:                                                                                \
+    return x_f16 ? mmv_t<TT, false>(blob, rows, cols, x, n_tok, y, st)                    \
+                 : mmv_t<TT, true>(blob, rows, cols, x, n_tok, y, st);
+    GQ_MMV_CASE(GQ_Q4_0)
+    GQ_MMV_CASE(GQ_Q5_0)
+    GQ_MMV_CASE(GQ_Q8_0)
+    GQ_MMV_CASE(GQ_Q4_K)
+    GQ_MMV_CASE(GQ_Q6_K)
+#undef GQ_MMV_CASE
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gq

@@ -148,13 +148,19 @@ def test_mfma_parity(t, xdt):
         check_matmul(y, blob, t, rows, cols, x, label=f"{t} n={n} {xdt}")
 
 
-def test_mfma_many_slabs_and_rows():
-    t, rows, cols = "q4_k", 300, 4096
+@pytest.mark.parametrize("t", gq.QUANT_TYPES)
+def test_mfma_many_slabs_and_rows(t):
+    """Rows split into many 16-row tiles and the columns into 16 slabs shared
+    by several waves; for the 32-weight types the last slab is partial
+    (4000 columns = 125 blocks)."""
+    rows, cols = 300, (4096 if QK[t] == 256 else 4000)
     _, blob = quantized(t, rows, cols, seed=32)
-    x = synth.activations(40, cols, seed=33, dtype="f16")
-    say("mfma q4_k 300x4096 n=40")
-    y = gq.matmul(to_dev(blob), t, rows, cols, to_dev(x)).cpu().numpy()
-    check_matmul(y, blob, t, rows, cols, x, label="q4_k 300x4096 n=40")
+    bd = to_dev(blob)
+    for n, xdt in ((8, "f16"), (9, "f16"), (40, "f16"), (5, "f32"), (40, "f32")):
+        say(f"mfma {t} {rows}x{cols} n={n} x={xdt}")
+        x = synth.activations(n, cols, seed=33 + n, dtype=xdt)
+        y = gq.matmul(bd, t, rows, cols, to_dev(x)).cpu().numpy()
+        check_matmul(y, blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
 
 
 # ---------------------------------------------------------------- exact special cases
