@@ -12,7 +12,7 @@ namespace {
 constexpr int64_t kDim = (int64_t)1 << 31;       // rows, cols, n_tok < 2^31
 constexpr int64_t kBytes = (int64_t)1 << 47;     // any one buffer < 2^47 bytes
 constexpr int64_t kMaxColsGemv = 16384;          // x staged in 64 KB of LDS
-constexpr int64_t kMaxColsBatch = (int64_t)1 << 24;  // n_tok >= 2: 16 tokens of x in 32-bit offsets
+constexpr int64_t kMaxColsBatch = (int64_t)1 << 21;  // n_tok >= 2: 128 tokens of x in 31-bit offsets
 constexpr int64_t kMaxTokens = (int64_t)1 << 22;  // matrix-core grid.y = n_tok / 64 < 65536
 constexpr int64_t kSmallBatch = 64;               // n_tok up to this: weight-stream kernel
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // dequant / quantize grid.x < 2^31
@@ -107,7 +107,7 @@ int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t c
   if (n_tok == 1) return hip_status(gq::launch_gemv(ggml_type, weight_blob, rows, cols, x, xf16, y, st));
   if (n_tok <= kSmallBatch)
     return hip_status(gq::launch_mmv(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
-  return hip_status(gq::launch_mfma(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
+  return hip_status(gq::launch_gemm(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
 }
 
 int gq_matmul(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols, const void* x,

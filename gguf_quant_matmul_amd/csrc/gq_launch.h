@@ -16,9 +16,7 @@ hipError_t launch_gemv(int type, const void* blob, int64_t rows, int64_t cols, c
 // Small batches: the weight stream on the matrix cores, 16 tokens per pass.
 hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                       bool x_f16, float* y, int64_t n_tok, hipStream_t st);
-// Larger batches: weights decoded once per 16..128-token pass, reused for
-// every token on the matrix cores.
-hipError_t launch_mfma(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
+// Prefill-sized batches: tiled fp16 GEMM with the weights decoded per tile.
+hipError_t launch_gemm(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, int64_t n_tok, hipStream_t st);
-
 }  // namespace gq

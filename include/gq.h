@@ -82,8 +82,8 @@ enum {
  *
  * Limits: rows, cols and n_tok below 2^31; rows*RB, n_tok*cols and
  * n_tok*rows below 2^47; cols <= 16384 at n_tok = 1 (x is staged in 64 KB of
- * LDS); cols <= 2^24 at n_tok >= 2 (16 tokens of x are addressed with 32-bit
- * offsets); n_tok <= 2^22; rows*cols <= 2^40 for gq_dequant and gq_quantize.
+ * LDS); cols <= 2^21 at n_tok >= 2 (a tile of 128 tokens of x is addressed
+ * with 31-bit offsets); n_tok <= 2^22; rows*cols <= 2^40 for gq_dequant and gq_quantize.
  * Beyond a limit the call returns GQ_EOVERFLOW.
  */
 
@@ -119,9 +119,12 @@ int gq_matmul(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols
  * both are multiplied: about 22 of x's 24 significant bits are kept for
  * |x| >= 2^-3, values below that lose relative precision as lo reaches fp16's
  * subnormal range (absolute error <= 2^-25), and |x| must stay below 65504.
- * fp16 activations are used as given.  Decoded weights enter the products as
- * exact integers except for Q6_K, whose sc*(q-32) is rounded to fp16 when its
- * magnitude exceeds 2048 (relative error <= 2^-11).
+ * fp16 activations are used as given.  Up to 64 tokens the decoded weights
+ * enter the products as exact integers (scaled by d and dmin in fp32), except
+ * Q6_K's sc*(q-32), rounded to fp16 when its magnitude exceeds 2048; beyond 64
+ * tokens each weight enters as RNE_fp16 of its fp32 dequant (the value
+ * gq_dequant returns with out_type GQ_F16).  Either way the relative error of
+ * a product is at most 2^-11.
  */
 int gq_matmul_ex(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
                  const void *x, int x_type, float *y, int64_t n_tok, void *stream);
