@@ -10,9 +10,14 @@
 //     every weight is decoded with one fp32 fma and rounded to fp16 by
 //     v_fma_mix (relative error <= 2^-11 per weight, inside the stated
 //     1e-3 of sum |w*x|);
-//   * workgroup tile 128 tokens x 128 weight rows, K steps of 64 columns;
-//     4 waves of 64 x 64, each 2 x 2 v_mfma_f32_32x32x16_f16;
-//   * both operands live in LDS, double-buffered, 16-byte chunks XOR-
+//   * workgroup tile 128 tokens x 256 weight rows, K steps of 64 columns;
+//     8 waves, each owning 32 weight rows x all 128 tokens (4 x 1
+//     v_mfma_f32_32x32x16_f16 per 16 columns);
+//   * each wave decodes its own B fragments straight into registers (no
+//     redundancy, and no LDS writes for B: LDS stores run at about a third
+//     of the LDS read rate here); step i + 1 is decoded while the matrix
+//     cores run step i;
+//   * activations are staged in LDS, double-buffered, 16-byte chunks XOR-
 //     swizzled per row so fragment reads and tile writes are conflict-free;
 //   * the raw weight bytes and activations of the next D K-steps are in
 //     flight in a register ring (loads complete in issue order, so both
@@ -21,6 +26,8 @@
 //     hi), and both pass through the matrix op;
 //   * tiles are mapped so that the token tiles of one weight-row tile run on
 //     one XCD (workgroups go round-robin over the 8 XCDs) and share its L2.
+#include <type_traits>
+
 #include "gq_device.h"
 #include "gq_launch.h"
 
@@ -30,8 +37,17 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int TILE = BM * BK * 2;            // bytes of one fp16 tile (128 rows x 64)
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+constexpr int BM = 128, BK = 64;
+constexpr int ROWB = BK * 2;                 // bytes of one tile row (64 fp16)
 
 // 16-byte chunk c (0..7) of tile row t lives at t * 128 + 16 * (c ^ swz(t)).
 // Any 16 consecutive rows then use 16 distinct chunk slots of a 256-byte
@@ -51,13 +67,16 @@ __device__ __forceinline__ uint32_t h2pack(float a, float b) {
 // fp16 weights.
 template <int T> struct BR;
 template <> struct BR<GQ_Q4_K> {
+  static constexpr bool kHeader = true;      // header shared by a super-block's 4 steps
   u32x4 hd, q;
+  template <bool HDR = true>
   __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
     const int vo = ok ? vrow + (sg >> 3) * 144 : kOobOff;
-    hd = bld16(R, vo, 0);
+    if constexpr (HDR) hd = bld16(R, vo, 0);
     q = bld16(R, vo + 16 * (sg & 7), 16);
   }
-  __device__ void decode(int sg, u32x4 out[4]) const {
+  __device__ void decode(int sg, u32x4 out[4]) const { decode(sg, hd, out); }
+  __device__ void decode(int sg, const u32x4& hd, u32x4 out[4]) const {
     const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
     const uint32_t f = q4k_pair(hd.y, hd.z, hd.w, sg & 7);
     const float a = d * (float)(f & 63u), nb = -(dmin * (float)(f >> 6));
@@ -75,9 +94,11 @@ template <> struct BR<GQ_Q4_K> {
   }
 };
 template <> struct BR<GQ_Q6_K> {
+  static constexpr bool kHeader = false;
   u32x4 ql;
   u32x2 qh;
   uint32_t sc, d;
+  template <bool HDR = true>
   __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
     const int vo = ok ? vrow + (sg >> 3) * 210 : kOobOff;
     const int G = sg & 7;
@@ -106,8 +127,10 @@ template <> struct BR<GQ_Q6_K> {
   }
 };
 template <> struct BR<GQ_Q8_0> {
+  static constexpr bool kHeader = false;
   u32x4 c0, c1;
   uint32_t d;
+  template <bool HDR = true>
   __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
     const int vo = ok ? vrow + sg * 34 : kOobOff;
     d = bld2(R, vo, 0);
@@ -126,8 +149,10 @@ template <> struct BR<GQ_Q8_0> {
   }
 };
 template <int T> struct BR4 {                // Q4_0 and Q5_0
+  static constexpr bool kHeader = false;
   u32x4 c;
   uint32_t qh, d;
+  template <bool HDR = true>
   __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
     const int vo = ok ? vrow + sg * Geo<T>::BB : kOobOff;
     d = bld2(R, vo, 0);
@@ -162,23 +187,31 @@ template <int T> struct BR4 {                // Q4_0 and Q5_0
 template <> struct BR<GQ_Q4_0> : BR4<GQ_Q4_0> {};
 template <> struct BR<GQ_Q5_0> : BR4<GQ_Q5_0> {};
 
-// Activations: the thread's share of one 128 x 64 tile.  fp16: load i, thread
-// tid covers row (256 i + tid) / 8, chunk (256 i + tid) % 8 (8 lanes read one
-// 128-byte line).  fp32: load i covers row (256 i + tid) / 16, 4 columns.
-template <bool XLO> struct AR {
-  u32x4 v[XLO ? 8 : 4];
+// Activations: the thread's share of one 128 x 64 tile (NT threads).  fp16:
+// load i, thread tid covers row (NT i + tid) / 8, chunk (NT i + tid) % 8 (8
+// lanes read one 128-byte line).  fp32: row (NT i + tid) / 16, 4 columns.
+template <bool XLO, int NT> struct AR {
+  static constexpr int N = (XLO ? 2048 : 1024) / NT;
+  u32x4 v[N];
 };
 
 }  // namespace
 
+#ifndef GQ_GEMM_VPM
+#define GQ_GEMM_VPM 5                         // VALU instructions placed after each MFMA
+#endif
+
 template <int T, bool XLO, int D>
-__global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ blob, int rows, int cols,
+__global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, int rows, int cols,
                                               int rb, const void* __restrict__ xv, int n,
                                               float* __restrict__ y, int tn, int tm) {
+  constexpr int BN = 256, NT = 512;          // 8 waves, 32 weight rows each
   constexpr int NA = XLO ? 2 : 1;            // activation planes: hi (and lo)
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][NA][TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][TILE];
+  constexpr int ATILE = BM * ROWB;
+  static_assert(D % 2 == 0, "even ring depth: LDS buffer parity is static");
+  __shared__ __attribute__((aligned(16))) uint8_t As[2 * NA * ATILE];
   constexpr int ES = XLO ? 4 : 2;
+  constexpr int NL = AR<XLO, NT>::N;         // activation loads per thread per step
 
   // tile q of XCD x covers tiles x * per .. ; token tiles of a row tile adjacent
   const int total = tn * tm, per = (total + 7) >> 3;
@@ -187,33 +220,47 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ blob, 
   const int n0 = (q / tm) * BN, m0 = (q % tm) * BM;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w & 1, wn = w >> 1;
   const int nr = min(BN, rows - n0), nt = min(BM, n - m0);
   const __amdgpu_buffer_rsrc_t WR = make_rsrc(blob + (int64_t)n0 * rb, (uint32_t)(nr * rb));
   const __amdgpu_buffer_rsrc_t XR =
       make_rsrc((const uint8_t*)xv + (int64_t)m0 * cols * ES, (uint32_t)(nt * cols * ES));
   const int nk = (cols + BK - 1) / BK;
   const int nseg = cols >> 5;
-  const int br = tid >> 1, bh = tid & 1;     // weight row and half this thread decodes
-  const int vrow = br * rb;
+  // B fragment lane: weight row 32 w + fr of the tile; k half fk = the
+  // 32-column segment 2 * step + fk of the row (its chunk ks feeds MFMA ks)
+  const int fr = lane & 31, fk = lane >> 5;
+  const int vrow = (32 * w + fr) * rb;
 
-  auto load = [&](AR<XLO>& a, BR<T>& b, int s) {
-    const int sg = 2 * s + bh;
-    b.load(WR, vrow, sg, sg < nseg);
+  // loop-invariant offsets
+  int xo[NL], aw[NL];                        // activation load i: global / LDS offsets
 #pragma unroll
-    for (int i = 0; i < (XLO ? 8 : 4); i++) {
-      const int id = 256 * i + tid;
-      const int t = XLO ? (id >> 4) : (id >> 3);
-      const int col = s * BK + (XLO ? 4 * (id & 15) : 8 * (id & 7));
-      a.v[i] = bld16(XR, col < cols ? (t * cols + col) * ES : kOobOff, 0);
-    }
+  for (int i = 0; i < NL; i++) {
+    const int id = NT * i + tid;
+    const int t = XLO ? (id >> 4) : (id >> 3);
+    const int c = XLO ? 4 * (id & 15) : 8 * (id & 7);
+    xo[i] = (t * cols + c) * ES;
+    aw[i] = XLO ? tslot(t, (id & 15) >> 1) + 8 * (id & 1) : tslot(t, id & 7);
+  }
+  const int xc = XLO ? 4 * (tid & 15) : 8 * (tid & 7);   // column of every load
+  int fo[BK / 16];                           // A fragment of MFMA ks: chunk 4 fk + ks
+#pragma unroll
+  for (int ks = 0; ks < BK / 16; ks++) fo[ks] = fr * ROWB + (((4 * fk + ks) ^ swz(fr)) << 4);
+
+  // With a 4-deep ring, ring slot u always holds steps = u mod 4, so only
+  // slot 0 (the first step of each super-block) loads the Q4_K header.
+  constexpr bool SHARE = BR<T>::kHeader && D == 4;
+  auto load = [&](AR<XLO, NT>& a, BR<T>& b, int s, auto hdr) {
+    const int sg = 2 * s + fk;
+    b.template load<decltype(hdr)::value>(WR, vrow, sg, sg < nseg);
+    const int col = s * BK + xc;
+#pragma unroll
+    for (int i = 0; i < NL; i++) a.v[i] = bld16(XR, col < cols ? xo[i] + s * BK * ES : kOobOff, 0);
   };
-  auto stage = [&](const AR<XLO>& a, const BR<T>& b, int s, int buf) {
+  auto stage_a = [&](const AR<XLO, NT>& a, int buf) {
+    uint8_t* const A0 = As + buf * NA * ATILE;
 #pragma unroll
-    for (int i = 0; i < (XLO ? 8 : 4); i++) {
-      const int id = 256 * i + tid;
+    for (int i = 0; i < NL; i++) {
       if constexpr (XLO) {
-        const int t = id >> 4, c4 = id & 15;
         const f32x4 f = __builtin_bit_cast(f32x4, a.v[i]);
         float hi[4], lo[4];
 #pragma unroll
@@ -221,85 +268,104 @@ __global__ void __launch_bounds__(256) k_gemm(const uint8_t* __restrict__ blob, 
           hi[e] = (float)(_Float16)f[e];
           lo[e] = f[e] - hi[e];
         }
-        const int o = tslot(t, c4 >> 1) + 8 * (c4 & 1);
-        *reinterpret_cast<u32x2*>(&As[buf][0][o]) = u32x2{h2pack(hi[0], hi[1]), h2pack(hi[2], hi[3])};
-        *reinterpret_cast<u32x2*>(&As[buf][1][o]) = u32x2{h2pack(lo[0], lo[1]), h2pack(lo[2], lo[3])};
+        *reinterpret_cast<u32x2*>(A0 + aw[i]) = u32x2{h2pack(hi[0], hi[1]), h2pack(hi[2], hi[3])};
+        *reinterpret_cast<u32x2*>(A0 + ATILE + aw[i]) = u32x2{h2pack(lo[0], lo[1]), h2pack(lo[2], lo[3])};
       } else {
-        *reinterpret_cast<u32x4*>(&As[buf][0][tslot(id >> 3, id & 7)]) = a.v[i];
+        *reinterpret_cast<u32x4*>(A0 + aw[i]) = a.v[i];
       }
     }
-    u32x4 dq[4];
-    b.decode(2 * s + bh, dq);
-#pragma unroll
-    for (int c = 0; c < 4; c++) *reinterpret_cast<u32x4*>(&Bs[buf][tslot(br, 4 * bh + c)]) = dq[c];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4];
 #pragma unroll
-  for (int i = 0; i < 2; i++)
-#pragma unroll
-    for (int j = 0; j < 2; j++) acc[i][j] = f32x16{};
+  for (int i = 0; i < 4; i++) acc[i] = f32x16{};
 
-  AR<XLO> ra[D];
+  AR<XLO, NT> ra[D];
   BR<T> rw[D];
-#pragma unroll
-  for (int i = 0; i < D; i++) {
-    load(ra[i], rw[i], i);                   // issued in ring order
+  u32x4 bq[2][4];                            // decoded B fragments, double-buffered
+  u32x4 hcur = {0, 0, 0, 0};                 // header of the current super-block (SHARE)
+  auto hflag = [](auto u) { return std::integral_constant<bool, !SHARE || decltype(u)::value == 0>{}; };
+  auto decode = [&](BR<T>& b, int s, u32x4 out[4], auto u) {
+    if constexpr (SHARE) {
+      if constexpr (decltype(u)::value == 0) hcur = b.hd;
+      b.decode(2 * s + fk, hcur, out);
+    } else {
+      b.decode(2 * s + fk, out);
+    }
+  };
+  static_for<D>([&](auto u) {
+    load(ra[u], rw[u], u, hflag(u));         // issued in ring order
     __builtin_amdgcn_sched_barrier(0);
-  }
-  stage(ra[0], rw[0], 0, 0);
+  });
+  stage_a(ra[0], 0);
+  decode(rw[0], 0, bq[0], std::integral_constant<int, 0>{});
   __builtin_amdgcn_sched_barrier(0);
-  load(ra[0], rw[0], D);
+  load(ra[0], rw[0], D, hflag(std::integral_constant<int, 0>{}));
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
-  const int fr = lane & 31, fk = lane >> 5;  // fragment row, k half
+  // Steps past the last read zeros (masked loads), so every unrolled step
+  // runs unguarded and adds exactly nothing.
   for (int i0 = 0; i0 < nk; i0 += D) {
-#pragma unroll
-    for (int u = 0; u < D; u++) {
+    static_for<D>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
       const int i = i0 + u;
-      if (i < nk) {                          // uniform
-        const int buf = i & 1;
+      constexpr int buf = u & 1;             // i0 is a multiple of D, D even
+      const uint8_t* const A0 = As + buf * NA * ATILE;
+      constexpr int sl = (u + 1) % D;        // ring slot of step i + 1
+      const std::integral_constant<int, sl> slc{};
+      // decode step i + 1 while the matrix cores run step i
+      decode(rw[sl], i + 1, bq[buf ^ 1], slc);
+      // A fragments of sub-step ks + 1 are read while sub-step ks multiplies
+      f16x8 af[2][NA][4];
+      auto read_a = [&](int ks, f16x8 (&f)[NA][4]) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ks++) {
-          f16x8 af[NA][2], bf[2];
+        for (int mi = 0; mi < 4; mi++)
 #pragma unroll
-          for (int mi = 0; mi < 2; mi++)
+          for (int p = 0; p < NA; p++)
+            f[p][mi] = *reinterpret_cast<const f16x8*>(A0 + p * ATILE + mi * 32 * ROWB + fo[ks]);
+      };
+      read_a(0, af[0]);
 #pragma unroll
-            for (int p = 0; p < NA; p++)
-              af[p][mi] = *reinterpret_cast<const f16x8*>(&As[buf][p][tslot(wm * 64 + mi * 32 + fr, 2 * ks + fk)]);
+      for (int ks = 0; ks < BK / 16; ks++) {
+        if (ks + 1 < BK / 16) read_a(ks + 1, af[(ks + 1) & 1]);
+        const f16x8 bf = __builtin_bit_cast(f16x8, bq[buf][ks]);
 #pragma unroll
-          for (int ni = 0; ni < 2; ni++)
-            bf[ni] = *reinterpret_cast<const f16x8*>(&Bs[buf][tslot(wn * 64 + ni * 32 + fr, 2 * ks + fk)]);
+        for (int mi = 0; mi < 4; mi++)
 #pragma unroll
-          for (int mi = 0; mi < 2; mi++)
-#pragma unroll
-            for (int ni = 0; ni < 2; ni++)
-#pragma unroll
-              for (int p = 0; p < NA; p++)
-                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[p][mi], bf[ni], acc[mi][ni], 0, 0, 0);
-        }
-        if (i + 1 < nk) stage(ra[(u + 1) % D], rw[(u + 1) % D], i + 1, buf ^ 1);
+          for (int p = 0; p < NA; p++)
+            acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][p][mi], bf, acc[mi], 0, 0, 0);
       }
+      stage_a(ra[sl], buf ^ 1);
+#ifndef GQ_GEMM_NO_PIPE
+      // Shape of this step for the scheduler: the first fragments, then each
+      // MFMA followed by a share of the decode VALU and the next fragment
+      // read, so the matrix cores, VALU and LDS overlap within every wave.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * NA, 0);   // DS read
+#pragma unroll
+      for (int k = 0; k < 16 * NA; k++) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, GQ_GEMM_VPM, 0);   // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, NL * NA, 0);  // DS write: stage last
+#endif
       __builtin_amdgcn_sched_barrier(0);
-      load(ra[(u + 1) % D], rw[(u + 1) % D], i + 1 + D);   // past the last step: zeros
+      load(ra[sl], rw[sl], i + 1 + D, hflag(slc));   // past the last step: zeros
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
-    }
+    });
   }
 
-  // D lane l, register v: weight row l % 32 of the fragment, token
-  // 8 (v / 4) + 4 (l / 32) + v % 4
+  // D lane l, register v: weight row 32 w + l % 32, token 32 mi + 8 (v / 4) +
+  // 4 (l / 32) + v % 4
+  const int r = 32 * w + fr;
 #pragma unroll
-  for (int mi = 0; mi < 2; mi++)
+  for (int mi = 0; mi < 4; mi++)
 #pragma unroll
-    for (int ni = 0; ni < 2; ni++) {
-      const int r = wn * 64 + ni * 32 + fr;
-#pragma unroll
-      for (int v = 0; v < 16; v++) {
-        const int t = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
-        if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = acc[mi][ni][v];
-      }
+    for (int v = 0; v < 16; v++) {
+      const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
+      if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = acc[mi][v];
     }
 }
 
@@ -308,13 +374,14 @@ namespace {
 template <int T, bool XLO>
 hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
                   hipStream_t st) {
+  constexpr int BN = 256;
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t es = XLO ? 4 : 2;
   if ((int64_t)BN * rb >= kOobOff || (int64_t)BM * cols * es >= kOobOff) return hipErrorInvalidValue;
   const int64_t tn = (rows + BN - 1) / BN, tm = (n + BM - 1) / BM;
   if (tn * tm >= ((int64_t)1 << 31) / 8) return hipErrorInvalidValue;
   const int64_t grid = (tn * tm + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm<T, XLO, XLO ? 2 : 3>), dim3((unsigned)grid), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_gemm<T, XLO, XLO ? 2 : 4>), dim3((unsigned)grid), dim3(512), 0, st,
                      (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tn,
                      (int)tm);
   return hipGetLastError();
