@@ -27,8 +27,9 @@ Method:
     the same layer, the oracle quantizing its own blobs from the same draws.
 
 Prints one JSON line.  `--profile-launches N` instead runs N plain (ungraphed)
-launches of each layer matrix plus a device copy of known size, for
-rocprofv3 kernel traces and counters.
+launches of each layer matrix plus a device copy of known size, and
+`--profile-gemm N` N plain launches of the 512-token GEMM, for rocprofv3
+kernel traces and counters.
 """
 from __future__ import annotations
 
@@ -50,6 +51,8 @@ FP16_PEAK_TFLOPS = 2500.0
 CACHE_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4k_decode_layer_counters.md")
 GEMV_SRC = os.path.join(ROOT, "gguf_quant_matmul_amd", "csrc", "k_gemv.hip")
+GEMM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_q4k_11008x4096_n512.md")
+GEMM_SRC = os.path.join(ROOT, "gguf_quant_matmul_amd", "csrc", "k_gemm.hip")
 
 # (name, type, [(part, rows)], cols): parts are the original matrices, stored
 # one after another (row-major blobs concatenate row-wise).
@@ -72,6 +75,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--no-sweep", action="store_true", help="skip the secondary shapes")
+    p.add_argument("--profile-gemm", type=int, default=0, metavar="N",
+                   help="only run N plain launches of the 512-token GEMM (for rocprofv3)")
     p.add_argument("--profile-launches", type=int, default=0)
     return p.parse_args()
 
@@ -182,6 +187,22 @@ def traffic_from_profile(kernel_bytes):
     return float(m_b.group(1))
 
 
+def gemm_fetch_from_profile():
+    """HBM bytes fetched per launch of the 512-token GEMM, from the committed
+    counter summary, or None when that summary was taken on other source."""
+    try:
+        text = open(GEMM_TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m_sha = re.search(r"k_gemm\.hip sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"fetch_bytes_per_launch:\s*(\d+)", text)
+    if not (m_sha and m_b):
+        return None
+    if hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest() != m_sha.group(1):
+        return None
+    return float(m_b.group(1))
+
+
 def cpu_baseline(layer_mats):
     import numpy as np
     import oracle
@@ -273,6 +294,17 @@ def main():
 
     gq.lib()
     torch.cuda.init()
+    if args.profile_gemm:
+        m = Mat("gemm q4_k 11008x4096 n=512", "q4_k", [("w", 11008)], 4096, seed=9000, ncopies=1,
+                n_tok=512, x_dtype="f16")
+        m.ensure_copies(2 * CACHE_BYTES)
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for i in range(args.profile_gemm):
+            m.launch(i, sp)
+        torch.cuda.synchronize()
+        log(f"profile: {args.profile_gemm} launches of {m.name}")
+        return
     layer_bytes = sum(gq.row_bytes(t, c) * sum(r for _, r in parts) for _, t, parts, c in LAYER)
     ncopy = max(2, -(-(2 * CACHE_BYTES + CACHE_BYTES // 2) // layer_bytes))
     log(f"setup: {len(LAYER)} launches per step, {layer_bytes} blob bytes, {ncopy} rotating copies")
@@ -327,7 +359,9 @@ def main():
                      "value": round(tf * 1e3, 1), "unit": "GFLOP/s", "us_per_launch": g["us"],
                      "roofline": {"bound": "mfma", "achieved": tf, "peak": FP16_PEAK_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(tf / FP16_PEAK_TFLOPS, 4),
-                                  "traffic": None}}
+                                  "traffic": gemm_fetch_from_profile(),
+                                  "traffic_note": "HBM bytes fetched per launch (FETCH_SIZE, "
+                                                  "calibrated); writes not included"}}
 
     cpu = None
     if not args.no_cpu:

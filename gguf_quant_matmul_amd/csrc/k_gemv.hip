@@ -16,12 +16,8 @@
 //     (Hitchhiker's Guide §11.2, w = (d*sc)*q - dmin*m; for Q6_K the offset
 //     32 plays the min); the 32-weight types convert each code to the signed
 //     q - offset so every product is exact relative to w; fp32 accumulation;
-//   * two persistent workgroups per CU (each stages all of x, so more would
-//     multiply that traffic) deal (row group, pass) items round-robin to their
-//     waves, which keep the next item's weights in flight; each 32-weight half
-//     dot is 8 independent 4-term chains; row sums use the DPP network.
-#include <algorithm>
-
+//   * persistent workgroups (as many as fit on the chip) loop over groups of
+//     rows with the next group's loads in flight; row sums use the DPP network.
 #include "gq_device.h"
 #include "gq_launch.h"
 
@@ -59,13 +55,12 @@ template <> struct Slice<GQ_Q4_K> {           // sub-blocks 2j, 2j+1 of a super-
   }
   __device__ float dot(int h, const float* x, const float* xs, int j) const {
     const u32x4 q = h ? q1 : q0;              // sub-block 2j + h
-    float sp[4], tp[4];                       // 8 short chains, not 2 long ones
+    float s = 0.f, t = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {             // low nibbles: elements 4k.., high: 16+4k..
-      sp[k] = dot4u(q[k] & 0x0F0F0F0Fu, x + 4 * k, 0.f);
-      tp[k] = dot4u((q[k] >> 4) & 0x0F0F0F0Fu, x + 16 + 4 * k, 0.f);
+      s = dot4u(q[k] & 0x0F0F0F0Fu, x + 4 * k, s);
+      t = dot4u((q[k] >> 4) & 0x0F0F0F0Fu, x + 16 + 4 * k, t);
     }
-    const float s = (sp[0] + sp[1]) + (sp[2] + sp[3]), t = (tp[0] + tp[1]) + (tp[2] + tp[3]);
     // (scale, min) of sub-blocks 2j, 2j+1: the 24 bits at bit 24j of the
     // 96-bit field stream in header bytes 4..15
     const uint32_t lo = (j <= 1) ? hd.y : (j == 2) ? hd.z : hd.w;
@@ -92,16 +87,15 @@ template <> struct Slice<GQ_Q6_K> {           // 32-weight groups 2j, 2j+1
     // group 2j + g; unsigned codes q = low4 | high2 << 4; per 16-weight
     // quarter sum((q - 32) * x) = sum(q * x) - 32 * sum(x)
     const u32x4 L = g ? l1 : l0;
-    float p0[4], p1[4];                       // 8 short chains, not 2 long ones
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       const uint32_t H = h[2 * g + (k & 1)];
       const uint32_t lo = (L[k] & 0x0F0F0F0Fu) | q6k_hi(H, k >> 1);
       const uint32_t hi = ((L[k] >> 4) & 0x0F0F0F0Fu) | q6k_hi(H, 2 + (k >> 1));
-      p0[k] = dot4u(lo, x + 4 * k, 0.f);
-      p1[k] = dot4u(hi, x + 16 + 4 * k, 0.f);
+      s0 = dot4u(lo, x + 4 * k, s0);
+      s1 = dot4u(hi, x + 16 + 4 * k, s1);
     }
-    const float s0 = (p0[0] + p0[1]) + (p0[2] + p0[3]), s1 = (p1[0] + p1[1]) + (p1[2] + p1[3]);
     const uint32_t sc2 = sc >> (16 * g);
     const float r = fmaf(sb1(sc2), fmaf(-32.f, xs[1], s1), sb0(sc2) * fmaf(-32.f, xs[0], s0));
     return h2f(d) * r;
@@ -121,13 +115,12 @@ template <> struct Slice<GQ_Q8_0> {           // blocks 2*sl, 2*sl+1
     c[3] = bld16(r, vo, 52);
   }
   __device__ float dot(int h, const float* x, const float*, int) const {
-    float pa[4], pb[4];                       // 8 short chains, not 2 long ones
+    float a = 0.f, b = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      pa[k] = dot4s(c[2 * h][k], x + 4 * k, 0.f);
-      pb[k] = dot4s(c[2 * h + 1][k], x + 16 + 4 * k, 0.f);
+      a = dot4s(c[2 * h][k], x + 4 * k, a);
+      b = dot4s(c[2 * h + 1][k], x + 16 + 4 * k, b);
     }
-    const float a = (pa[0] + pa[1]) + (pa[2] + pa[3]), b = (pb[0] + pb[1]) + (pb[2] + pb[3]);
     return h2f(h ? d1 : d0) * (a + b);
   }
 };
@@ -153,7 +146,7 @@ template <int T> struct SliceQ40Q50 {
   __device__ float dot(int h, const float* x, const float*, int) const {
     const u32x4 q = h ? q1 : q0;
     const uint32_t qh = h ? h1 : h0;
-    float pa[4], pb[4];                       // 8 short chains, not 2 long ones
+    float a = 0.f, b = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       uint32_t lo = q[k] & 0x0F0F0F0Fu, hi = (q[k] >> 4) & 0x0F0F0F0Fu;
@@ -161,10 +154,9 @@ template <int T> struct SliceQ40Q50 {
         lo |= spread4_bit4(qh >> (4 * k));
         hi |= spread4_bit4(qh >> (16 + 4 * k));
       }
-      pa[k] = dot4s(centre<OFF>(lo), x + 4 * k, 0.f);
-      pb[k] = dot4s(centre<OFF>(hi), x + 16 + 4 * k, 0.f);
+      a = dot4s(centre<OFF>(lo), x + 4 * k, a);
+      b = dot4s(centre<OFF>(hi), x + 16 + 4 * k, b);
     }
-    const float a = (pa[0] + pa[1]) + (pa[2] + pa[3]), b = (pb[0] + pb[1]) + (pb[2] + pb[3]);
     return h2f(h ? d1 : d0) * (a + b);
   }
 };
@@ -181,9 +173,9 @@ __device__ __forceinline__ int xswz(int f) {
 
 // Persistent GEMV.  LPR lanes cover a row's slices in each of npass passes
 // (a wave holds 64/LPR rows side by side when rows are short); each wave takes
-// R such row sets per group and walks its (group, pass) items with the next
-// D items' weights in flight, whatever the row length.
-template <int T, bool XF16, int LPR, int R, int XPT, int D>
+// R such row sets per group and walks its groups pass by pass, so the double
+// buffer holds one pass whatever the row length.
+template <int T, bool XF16, int LPR, int R, int XPT>
 __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, int rows,
                                               int cols, int rb, const void* __restrict__ xv,
                                               float* __restrict__ y) {
@@ -197,7 +189,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   const int npass = (nsl + LPR - 1) / LPR;
   const int cpad = nsl << 6;
   const int ngroups = (rows + ROWS - 1) / ROWS;
-  const int stride = gridDim.x * 4;        // groups are dealt to waves round-robin
+  const int stride = gridDim.x * 4;
   const int sub = lane / LPR;              // which of the side-by-side rows
   const int li = lane % LPR;
 
@@ -216,9 +208,9 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
     }
   }
 
-  // loads item (group grp, pass p) into w; lanes past the row's last slice
-  // repeat it (their sums are dropped); the descriptor ends at the matrix's
-  // last row, so groups past the end read zeros
+  Slice<T> cur[R], nxt[R];
+  // loads pass p of group grp into w; lanes past the row's last slice repeat
+  // it (their sums are dropped); the descriptor ends at the matrix's last row
   auto load_item = [&](Slice<T> (&w)[R], int grp, int p) {
     const int sl = min(p * LPR + li, nsl - 1);
     const int vo = Slice<T>::voff(sl);
@@ -230,19 +222,8 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
       w[k].load(rs, sub * rb + vo, sl & 3);
     }
   };
-  // Item j of this wave: group g0 + (j / npass) * stride, pass j % npass.
-  const int g0 = blockIdx.x * 4 + wave;
-  const int mygroups = g0 < ngroups ? (ngroups - 1 - g0) / stride + 1 : 0;
-  const int nitems = mygroups * npass;
-  auto item_group = [&](int j) { return g0 + (j / npass) * stride; };
-
-  // The first D items' weights are issued before x is staged, in ring order.
-  Slice<T> ring[D][R];
-#pragma unroll
-  for (int u = 0; u < D; u++) {
-    load_item(ring[u], item_group(u), u % npass);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  int g = blockIdx.x * 4 + wave;
+  if (g < ngroups) load_item(cur, g, 0);
 
   // x (fp32, zero-padded to whole slices) and its 16-column sums into LDS
 #pragma unroll
@@ -264,58 +245,50 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   }
   __syncthreads();
 
-  // Items stream through the D-deep ring.  Items past this wave's last read
-  // zeros and store nothing (their rows are past the matrix), so every
-  // unrolled step runs unguarded; the scheduling barriers keep the reloads
-  // in ring order (loads complete in issue order).
-  float acc[R];
+  for (; g < ngroups; g += stride) {
+    float acc[R];
 #pragma unroll
-  for (int k = 0; k < R; k++) acc[k] = 0.f;
-  if (nitems > 0) {
-    int j0 = 0;
-    do {
-#pragma unroll
-      for (int u = 0; u < D; u++) {
-        const int j = j0 + u;
-        const int p = j % npass;
-        const int s0 = p * LPR + li;
-        const int s = min(s0, nsl - 1);
-        const bool live = s0 < nsl;
-        const bool second = (2 * s + 1) * 32 < cols;   // the slice's second half is in the row
-#pragma unroll
-        for (int h = 0; h < 2; h++) {
-          float x[32];
-          const float* base = xsm + (s << 6);
-#pragma unroll
-          for (int c = 0; c < 8; c++) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(base + (((8 * h + c) ^ (s & 15)) << 2));
-            x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
-          }
-          const float2 xs2 = *reinterpret_cast<const float2*>(xsum + 4 * s + 2 * h);
-          const float xs[2] = {xs2.x, xs2.y};
-          const bool use = live && (h == 0 || second);
-#pragma unroll
-          for (int k = 0; k < R; k++) {
-            const float d = ring[u][k].dot(h, x, xs, s & 3);
-            acc[k] += use ? d : 0.f;
-          }
-        }
-        if (p == npass - 1) {                // the group's last pass: reduce and store
-          const int gq = item_group(j);
-#pragma unroll
-          for (int k = 0; k < R; k++) {
-            const float v = group_sum_dpp<LPR>(acc[k]);    // valid in lane LPR-1 of each group
-            const int r = gq * ROWS + k * RPW + sub;
-            if (li == LPR - 1 && r < rows) y[r] = v;
-            acc[k] = 0.f;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        load_item(ring[u], item_group(j + D), (j + D) % npass);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < R; k++) acc[k] = 0.f;
+    for (int p = 0; p < npass; p++) {
+      // next item: this group's next pass, else the next group's first
+      const bool more = (p + 1 < npass) || (g + stride < ngroups);
+      if (more) {
+        if (p + 1 < npass) load_item(nxt, g, p + 1);
+        else load_item(nxt, g + stride, 0);
       }
-      j0 += D;
-    } while (j0 < nitems);
+      const int s0 = p * LPR + li;
+      const int s = min(s0, nsl - 1);
+      const bool live = s0 < nsl;
+      const bool second = (2 * s + 1) * 32 < cols;   // the slice's second half is in the row
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        float x[32];
+        const float* base = xsm + (s << 6);
+#pragma unroll
+        for (int c = 0; c < 8; c++) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(base + (((8 * h + c) ^ (s & 15)) << 2));
+          x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+        }
+        const float2 xs2 = *reinterpret_cast<const float2*>(xsum + 4 * s + 2 * h);
+        const float xs[2] = {xs2.x, xs2.y};
+        const bool use = live && (h == 0 || second);
+#pragma unroll
+        for (int k = 0; k < R; k++) {
+          const float d = cur[k].dot(h, x, xs, s & 3);
+          acc[k] += use ? d : 0.f;
+        }
+      }
+      if (more) {
+#pragma unroll
+        for (int k = 0; k < R; k++) cur[k] = nxt[k];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < R; k++) {
+      const float v = group_sum_dpp<LPR>(acc[k]);          // valid in lane LPR-1 of each group
+      const int r = g * ROWS + k * RPW + sub;
+      if (li == LPR - 1 && r < rows) y[r] = v;
+    }
   }
 }
 
@@ -323,7 +296,8 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
 #define GQ_GEMV_R 1
 #endif
 
-static int cu_count() {
+template <typename K>
+static int resident_wgs(K kern, size_t lds) {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
@@ -331,24 +305,12 @@ static int cu_count() {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
   }
-  return cus;
-}
-
-template <typename K>
-static int resident_wgs(K kern, size_t lds) {
   int per = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)kern, 256, lds) != hipSuccess ||
       per < 1)
     per = 1;
-  return cu_count() * per;
+  return cus * per;
 }
-
-#ifndef GQ_GEMV_DEPTH
-#define GQ_GEMV_DEPTH 2                      // items in flight per wave
-#endif
-#ifndef GQ_GEMV_WG_PER_CU
-#define GQ_GEMV_WG_PER_CU 2                  // workgroups per CU (each stages its own x)
-#endif
 
 template <int T, bool XF16, int LPR, int R, int XPT>
 static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, const void* x,
@@ -356,16 +318,13 @@ static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, cons
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t cpad = (cols + 63) / 64 * 64;
   const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4;   // <= 68 KB for cols <= 16384
-  auto kern = k_gemv<T, XF16, LPR, R, XPT, GQ_GEMV_DEPTH>;
+  auto kern = k_gemv<T, XF16, LPR, R, XPT>;
   static size_t cap_lds = 0;               // resident workgroups for the last LDS size
   static int cap = 0;
   if (cap_lds != lds) { cap = resident_wgs(kern, lds); cap_lds = lds; }
-  // Few workgroups, each walking many items: every workgroup stages all of x
-  // in LDS, so more of them would multiply that traffic and its prologue.
-  const int64_t lim = std::min<int64_t>(cap, (int64_t)GQ_GEMV_WG_PER_CU * cu_count());
   const int64_t groups = (rows + (64 / LPR) * R - 1) / ((64 / LPR) * R);
   const int64_t wgs = (groups + 3) / 4;
-  dim3 grid((unsigned)(wgs < lim ? wgs : lim));
+  dim3 grid((unsigned)(wgs < cap ? wgs : cap));
   hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t*)blob, (int)rows, (int)cols,
                      (int)rb, x, y);
   return hipGetLastError();
