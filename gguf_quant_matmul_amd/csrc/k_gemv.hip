@@ -17,13 +17,16 @@
 //     32 plays the min); the 32-weight types convert each code to the signed
 //     q - offset so every product is exact relative to w; fp32 accumulation;
 //   * persistent workgroups (as many as fit on the chip) loop over groups of
-//     rows with the next group's loads in flight; row sums use the DPP network.
+//     rows with the next group's loads in flight; a wave's first two items
+//     are requested before x is staged, so the weight stream starts at launch
+//     (x's loads go first and are the only ones the staging waits for); row
+//     sums and the 16-column sums of x use the DPP network.
 #include "gq_device.h"
 #include "gq_launch.h"
 
 namespace gq {
 
-// acc + sum over the 4 bytes of w of (byte as unsigned / signed) * x[k]
+// acc + sum over the 4 bytes of w (as unsigned / signed integers) * x[k].
 __device__ __forceinline__ float dot4u(uint32_t w, const float* x, float acc) {
   acc = fmaf(ub0(w), x[0], acc);
   acc = fmaf(ub1(w), x[1], acc);
@@ -37,6 +40,20 @@ __device__ __forceinline__ float dot4s(uint32_t w, const float* x, float acc) {
   return fmaf(sb3(w), x[3], acc);
 }
 
+// The same as dot4u with each byte's convert and its FMA kept adjacent in one
+// asm block: the scheduler cannot hoist a whole slice's converts ahead of the
+// FMAs and hold 64 converted codes live at once (Q6_K's decode otherwise
+// needs enough registers to halve the waves per SIMD).
+__device__ __forceinline__ float dot4u_asm(uint32_t w, const float* x, float acc) {
+  float t;
+  asm("v_cvt_f32_ubyte0 %1, %2\n\tv_fmac_f32 %0, %1, %3\n\t"
+      "v_cvt_f32_ubyte1 %1, %2\n\tv_fmac_f32 %0, %1, %4\n\t"
+      "v_cvt_f32_ubyte2 %1, %2\n\tv_fmac_f32 %0, %1, %5\n\t"
+      "v_cvt_f32_ubyte3 %1, %2\n\tv_fmac_f32 %0, %1, %6"
+      : "+v"(acc), "=&v"(t)
+      : "v"(w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+  return acc;
+}
 // One lane's 64-weight slice of one row: raw registers and the slice dot in
 // two halves of 32 weights.  voff(sl) is slice sl's byte offset in its row;
 // j = sl % 4 its quarter of a K-quant block.  dot(h, x, xs, j) takes half h's
@@ -93,8 +110,8 @@ template <> struct Slice<GQ_Q6_K> {           // 32-weight groups 2j, 2j+1
       const uint32_t H = h[2 * g + (k & 1)];
       const uint32_t lo = (L[k] & 0x0F0F0F0Fu) | q6k_hi(H, k >> 1);
       const uint32_t hi = ((L[k] >> 4) & 0x0F0F0F0Fu) | q6k_hi(H, 2 + (k >> 1));
-      s0 = dot4u(lo, x + 4 * k, s0);
-      s1 = dot4u(hi, x + 16 + 4 * k, s1);
+      s0 = dot4u_asm(lo, x + 4 * k, s0);
+      s1 = dot4u_asm(hi, x + 16 + 4 * k, s1);
     }
     const uint32_t sc2 = sc >> (16 * g);
     const float r = fmaf(sb1(sc2), fmaf(-32.f, xs[1], s1), sb0(sc2) * fmaf(-32.f, xs[0], s0));
@@ -208,7 +225,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
     }
   }
 
-  Slice<T> cur[R], nxt[R];
+  Slice<T> cur[R];
   // loads pass p of group grp into w; lanes past the row's last slice repeat
   // it (their sums are dropped); the descriptor ends at the matrix's last row
   auto load_item = [&](Slice<T> (&w)[R], int grp, int p) {
@@ -225,26 +242,31 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   int g = blockIdx.x * 4 + wave;
   if (g < ngroups) load_item(cur, g, 0);
 
-  // x (fp32, zero-padded to whole slices) and its 16-column sums into LDS
+  // the second item's loads go out before x is staged too
+  Slice<T> nxt[R];
+  if (g < ngroups && (npass > 1 || g + stride < ngroups)) {
+    if (npass > 1) load_item(nxt, g, 1);
+    else load_item(nxt, g + stride, 0);
+  }
+
+  // x (fp32, zero-padded to whole slices) into LDS; each quad of lanes holds
+  // one 16-column group, summed on the DPP network
+  float* xsum = xsm + cpad;
 #pragma unroll
   for (int i = 0; i < XPT; i++) {
     const int c4 = (int)threadIdx.x + 256 * i;
-    if (c4 < (cpad >> 2))
-      *reinterpret_cast<f32x4*>(xsm + xswz(4 * c4)) = (c4 < nc4) ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __syncthreads();
-  float* xsum = xsm + cpad;
-  for (int q = threadIdx.x; q < (cpad >> 4); q += 256) {
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(xsm + xswz((q << 4) + 4 * c));
-      s += (v.x + v.y) + (v.z + v.w);
+    const f32x4 v = (c4 < nc4) ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+    float s = (v.x + v.y) + (v.z + v.w);
+    s += dpp_mov<0xB1>(s);
+    s += dpp_mov<0x4E>(s);
+    if (c4 < (cpad >> 2)) {
+      *reinterpret_cast<f32x4*>(xsm + xswz(4 * c4)) = v;
+      if ((c4 & 3) == 0) xsum[c4 >> 2] = s;
     }
-    xsum[q] = s;
   }
   __syncthreads();
 
+  bool first = true;
   for (; g < ngroups; g += stride) {
     float acc[R];
 #pragma unroll
@@ -252,10 +274,11 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
     for (int p = 0; p < npass; p++) {
       // next item: this group's next pass, else the next group's first
       const bool more = (p + 1 < npass) || (g + stride < ngroups);
-      if (more) {
+      if (more && !first) {
         if (p + 1 < npass) load_item(nxt, g, p + 1);
         else load_item(nxt, g + stride, 0);
       }
+      first = false;
       const int s0 = p * LPR + li;
       const int s = min(s0, nsl - 1);
       const bool live = s0 < nsl;
