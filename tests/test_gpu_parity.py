@@ -163,6 +163,48 @@ def test_mfma_many_slabs_and_rows(t):
         check_matmul(y, blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
 
 
+@pytest.mark.parametrize("t,rows,cols,n,xdt", [
+    ("q4_k", 256, 8192, 128, "f16"),     # one tile of 128 K steps
+    ("q6_k", 512, 4096, 200, "f32"),     # 4 tiles (2 x 2, the token tiles ragged), fp32 x
+    ("q8_0", 600, 2400, 96, "f16"),      # 3 x 1 tiles, 38 K steps: a partial last unit
+    ("q5_0", 300, 1056, 140, "f32"),     # 17 K steps, ragged rows and tokens
+])
+def test_gemm_few_tiles(t, rows, cols, n, xdt):
+    """Prefill shapes with few tiles and long or ragged K (a partial last
+    K step for the 32-weight types, ragged rows and token tiles): checked in
+    full against the oracle, and three calls in a row agree bit for bit."""
+    _, blob = quantized(t, rows, cols, seed=91)
+    bd = to_dev(blob)
+    say(f"gemm few tiles {t} {rows}x{cols} n={n} x={xdt}")
+    x = synth.activations(n, cols, seed=92, dtype=xdt)
+    xd = to_dev(x)
+    ys = [gq.matmul(bd, t, rows, cols, xd).cpu().numpy() for _ in range(3)]
+    for y in ys[1:]:
+        assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
+    check_matmul(ys[0], blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
+
+
+@pytest.mark.parametrize("t,rows,cols,n", [
+    ("q6_k", 4096, 11008, 512),          # 64 tiles x 172 K steps over every CU
+    ("q4_k", 11008, 4096, 768),          # 258 tiles: one more than a wave of 256
+])
+def test_gemm_partial_wave_full_size(t, rows, cols, n):
+    """Full-size prefill shapes whose tiles do not fill whole waves of CUs
+    (the FFN down projection's 64 tiles of 172 K steps; 258 tiles): sampled
+    rows against the oracle, and two calls bit-identical."""
+    _, blob = quantized(t, rows, cols, seed=93)
+    bd = to_dev(blob)
+    say(f"gemm partial wave {t} {rows}x{cols} n={n}")
+    x = synth.activations(n, cols, seed=94, dtype="f16")
+    xd = to_dev(x)
+    y0 = gq.matmul(bd, t, rows, cols, xd).cpu().numpy()
+    y1 = gq.matmul(bd, t, rows, cols, xd).cpu().numpy()
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    rng = np.random.default_rng(95)
+    idx = np.unique(np.concatenate([rng.choice(rows, 96, replace=False), np.r_[0:16, rows - 16:rows]]))
+    check_matmul(y0, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n}")
+
+
 # ---------------------------------------------------------------- exact special cases
 
 def _q8_unit_blob(codes):
