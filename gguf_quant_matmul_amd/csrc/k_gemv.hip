@@ -17,9 +17,8 @@
 //     32 plays the min); the 32-weight types convert each code to the signed
 //     q - offset so every product is exact relative to w; fp32 accumulation;
 //   * persistent workgroups (as many as fit on the chip) loop over groups of
-//     rows with the next group's loads in flight; a wave's first two items
-//     are requested before x is staged, so the weight stream starts at launch
-//     (x's loads go first and are the only ones the staging waits for); row
+//     rows with the next group's loads in flight (a wave's first two items
+//     go out before or after x is staged, by how many items it has); row
 //     sums and the 16-column sums of x use the DPP network.
 #include "gq_device.h"
 #include "gq_launch.h"
@@ -192,7 +191,7 @@ __device__ __forceinline__ int xswz(int f) {
 // (a wave holds 64/LPR rows side by side when rows are short); each wave takes
 // R such row sets per group and walks its groups pass by pass, so the double
 // buffer holds one pass whatever the row length.
-template <int T, bool XF16, int LPR, int R, int XPT>
+template <int T, bool XF16, int LPR, int R, int XPT, bool XFIRST>
 __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, int rows,
                                               int cols, int rb, const void* __restrict__ xv,
                                               float* __restrict__ y) {
@@ -239,15 +238,21 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
       w[k].load(rs, sub * rb + vo, sl & 3);
     }
   };
+  // A wave's first two items: requested before x is staged when the waves
+  // have many (the weight stream then starts at launch, and x's loads, issued
+  // first, are the only ones the staging waits for), after it when they
+  // have few (x then reaches every CU ahead of the weight traffic, and the
+  // kernel's span is the x latency plus one or two items' work).
   int g = blockIdx.x * 4 + wave;
-  if (g < ngroups) load_item(cur, g, 0);
-
-  // the second item's loads go out before x is staged too
   Slice<T> nxt[R];
-  if (g < ngroups && (npass > 1 || g + stride < ngroups)) {
-    if (npass > 1) load_item(nxt, g, 1);
-    else load_item(nxt, g + stride, 0);
-  }
+  auto first_two = [&]() {
+    if (g < ngroups) load_item(cur, g, 0);
+    if (g < ngroups && (npass > 1 || g + stride < ngroups)) {
+      if (npass > 1) load_item(nxt, g, 1);
+      else load_item(nxt, g + stride, 0);
+    }
+  };
+  if constexpr (!XFIRST) first_two();
 
   // x (fp32, zero-padded to whole slices) into LDS; each quad of lanes holds
   // one 16-column group, summed on the DPP network
@@ -265,6 +270,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
     }
   }
   __syncthreads();
+  if constexpr (XFIRST) first_two();
 
   bool first = true;
   for (; g < ngroups; g += stride) {
@@ -341,15 +347,22 @@ static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, cons
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t cpad = (cols + 63) / 64 * 64;
   const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4;   // <= 68 KB for cols <= 16384
-  auto kern = k_gemv<T, XF16, LPR, R, XPT>;
+  auto kern = k_gemv<T, XF16, LPR, R, XPT, false>;
   static size_t cap_lds = 0;               // resident workgroups for the last LDS size
-  static int cap = 0;
+  static int cap = 0;                      // (both orders use the same registers)
   if (cap_lds != lds) { cap = resident_wgs(kern, lds); cap_lds = lds; }
   const int64_t groups = (rows + (64 / LPR) * R - 1) / ((64 / LPR) * R);
   const int64_t wgs = (groups + 3) / 4;
   dim3 grid((unsigned)(wgs < cap ? wgs : cap));
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t*)blob, (int)rows, (int)cols,
-                     (int)rb, x, y);
+  // items of the wave with the most: x goes first when that is at most 2
+  const int64_t npass = ((cols + 63) / 64 + LPR - 1) / LPR;
+  const int64_t most = (groups + 4 * (int64_t)grid.x - 1) / (4 * (int64_t)grid.x) * npass;
+  if (most <= 2)
+    hipLaunchKernelGGL((k_gemv<T, XF16, LPR, R, XPT, true>), grid, dim3(256), lds, st,
+                       (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, y);
+  else
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t*)blob, (int)rows,
+                       (int)cols, (int)rb, x, y);
   return hipGetLastError();
 }
 
