@@ -163,6 +163,23 @@ def test_mfma_many_slabs_and_rows(t):
         check_matmul(y, blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
 
 
+@pytest.mark.parametrize("t,rows,cols,ns", [
+    ("q4_k", 16400, 512, ((8, "f16"), (16, "f16"), (5, "f32"), (40, "f16"))),
+    ("q6_k", 8200, 768, ((8, "f16"), (3, "f32"), (24, "f16"))),
+])
+def test_mmv_tall_matrices(t, rows, cols, ns):
+    """Small batches on tall matrices (over a thousand 16-row tiles, the last
+    one ragged) with fp16 and fp32 activations, one and several token
+    passes: checked in full against the oracle."""
+    _, blob = quantized(t, rows, cols, seed=96)
+    bd = to_dev(blob)
+    for n, xdt in ns:
+        say(f"mmv tall {t} {rows}x{cols} n={n} x={xdt}")
+        x = synth.activations(n, cols, seed=97 + n, dtype=xdt)
+        y = gq.matmul(bd, t, rows, cols, to_dev(x)).cpu().numpy()
+        check_matmul(y, blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
+
+
 @pytest.mark.parametrize("t,rows,cols,n,xdt", [
     ("q4_k", 256, 8192, 128, "f16"),     # one tile of 128 K steps
     ("q6_k", 512, 4096, 200, "f32"),     # 4 tiles (2 x 2, the token tiles ragged), fp32 x
