@@ -48,6 +48,8 @@ def lib():
         L.gq_matmul.restype = ci
         L.gq_matmul_ex.argtypes = [vp, ci, i64, i64, vp, ci, vp, i64, vp]
         L.gq_matmul_ex.restype = ci
+        L.gq_matmul_decode.argtypes = [vp, vp, ci, i64, i64, vp, ci, vp, ctypes.c_float, vp, vp]
+        L.gq_matmul_decode.restype = ci
         L.gq_dequant.argtypes = [vp, ci, i64, i64, vp, ci, vp]
         L.gq_dequant.restype = ci
         L.gq_quantize.argtypes = [vp, ci, i64, i64, vp, vp]
@@ -112,6 +114,31 @@ def matmul(blob, t, rows: int, cols: int, x, out=None, stream=None):
                             out.data_ptr(), n, _stream(stream))
     if rc:
         raise GQError(rc, "gq_matmul_ex")
+    return out
+
+
+def matmul_decode(blob, t, rows: int, cols: int, x, up=None, norm_weight=None, eps: float = 1e-5,
+                  out=None, stream=None):
+    """One token: y[rows] = W^ RMSNorm(x) (norm_weight given) or W^ x, or with
+    `up` (a second blob of the same type and shape) silu(W^ xin) * (U^ xin)."""
+    import torch
+    x = x.reshape(-1)
+    if x.dtype not in (torch.float32, torch.float16):
+        raise TypeError("x must be float32 or float16")
+    x = x.contiguous()
+    if norm_weight is not None:
+        if norm_weight.dtype != torch.float32:
+            raise TypeError("norm_weight must be float32")
+        norm_weight = norm_weight.contiguous()
+    if out is None:
+        out = torch.empty(rows, dtype=torch.float32, device=x.device)
+    xt = F16 if x.dtype == torch.float16 else F32
+    rc = lib().gq_matmul_decode(blob.data_ptr(), None if up is None else up.data_ptr(), _tid(t),
+                                rows, cols, x.data_ptr(), xt,
+                                None if norm_weight is None else norm_weight.data_ptr(),
+                                float(eps), out.data_ptr(), _stream(stream))
+    if rc:
+        raise GQError(rc, "gq_matmul_decode")
     return out
 
 

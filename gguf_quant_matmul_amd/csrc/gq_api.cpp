@@ -115,6 +115,31 @@ int gq_matmul(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols
   return gq_matmul_ex(weight_blob, ggml_type, rows, cols, x, GQ_F32, y, n_tok, stream);
 }
 
+int gq_matmul_decode(const void* weight_blob, const void* up_blob, int ggml_type, int64_t rows,
+                     int64_t cols, const void* x, int x_type, const float* norm_weight, float eps,
+                     float* y, void* stream) {
+  int64_t rb = 0;
+  int rc = check_matrix(ggml_type, rows, cols, &rb);
+  if (rc) return rc;
+  if (x_type != GQ_F32 && x_type != GQ_F16) return GQ_EINVAL_TYPE;
+  if (cols > kMaxColsGemv) return GQ_EOVERFLOW;
+  if (!(eps >= 0.f) || eps > 3.4e38f) return GQ_EINVAL_SHAPE;   // NaN and inf included
+  if (!weight_blob || !x || !y) return GQ_EINVAL_PTR;
+  if (!aligned16(weight_blob) || !aligned16(x) || !aligned16(y) ||
+      (up_blob && !aligned16(up_blob)) || (norm_weight && !aligned16(norm_weight)))
+    return GQ_EALIGN;
+  const int64_t xbytes = cols * (x_type == GQ_F16 ? 2 : 4);
+  const int64_t ybytes = rows * 4;
+  const int64_t wbytes = rows * rb;
+  if (overlap(x, xbytes, y, ybytes) || overlap(weight_blob, wbytes, y, ybytes) ||
+      (up_blob && overlap(up_blob, wbytes, y, ybytes)) ||
+      (norm_weight && overlap(norm_weight, cols * 4, y, ybytes)))
+    return GQ_EINVAL_PTR;
+  return hip_status(gq::launch_gemv_fused(ggml_type, weight_blob, up_blob, rows, cols, x,
+                                          x_type == GQ_F16, norm_weight, eps, y,
+                                          (hipStream_t)stream));
+}
+
 int gq_dequant(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols, void* out,
                int out_type, void* stream) {
   int64_t rb = 0;

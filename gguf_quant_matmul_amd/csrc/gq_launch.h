@@ -13,6 +13,11 @@ hipError_t launch_quantize(int type, const float* w, int64_t rows, int64_t cols,
 // One token (n_tok == 1): the bandwidth-bound GEMV family.
 hipError_t launch_gemv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, hipStream_t st);
+// One token with decode-layer fusions: RMSNorm of x first (norm_weight not
+// null), and/or silu(W x) * (U x) out (up_blob not null, same type and shape).
+hipError_t launch_gemv_fused(int type, const void* blob, const void* up_blob, int64_t rows,
+                             int64_t cols, const void* x, bool x_f16, const float* norm_weight,
+                             float eps, float* y, hipStream_t st);
 // Small batches: the weight stream on the matrix cores, 16 tokens per pass.
 hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                       bool x_f16, float* y, int64_t n_tok, hipStream_t st);

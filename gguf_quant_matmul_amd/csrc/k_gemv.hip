@@ -39,10 +39,11 @@ __device__ __forceinline__ float dot4s(uint32_t w, const float* x, float acc) {
   return fmaf(sb3(w), x[3], acc);
 }
 
-// The same as dot4u with each byte's convert and its FMA kept adjacent in one
-// asm block: the scheduler cannot hoist a whole slice's converts ahead of the
-// FMAs and hold 64 converted codes live at once (Q6_K's decode otherwise
-// needs enough registers to halve the waves per SIMD).
+// The same as dot4u / dot4s with each byte's convert and its FMA kept
+// adjacent in one asm block: the scheduler cannot hoist a whole slice's
+// converts ahead of the FMAs and hold 64 converted codes live at once (Q6_K's
+// decode, or any type's with two row sets, otherwise needs enough registers
+// to halve the waves per SIMD).
 __device__ __forceinline__ float dot4u_asm(uint32_t w, const float* x, float acc) {
   float t;
   asm("v_cvt_f32_ubyte0 %1, %2\n\tv_fmac_f32 %0, %1, %3\n\t"
@@ -53,6 +54,29 @@ __device__ __forceinline__ float dot4u_asm(uint32_t w, const float* x, float acc
       : "v"(w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
   return acc;
 }
+__device__ __forceinline__ float dot4s_asm(uint32_t w, const float* x, float acc) {
+  float t;
+  asm("v_cvt_f32_i32_sdwa %1, sext(%2) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_0\n\t"
+      "v_fmac_f32 %0, %1, %3\n\t"
+      "v_cvt_f32_i32_sdwa %1, sext(%2) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1\n\t"
+      "v_fmac_f32 %0, %1, %4\n\t"
+      "v_cvt_f32_i32_sdwa %1, sext(%2) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2\n\t"
+      "v_fmac_f32 %0, %1, %5\n\t"
+      "v_cvt_f32_i32_sdwa %1, sext(%2) dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3\n\t"
+      "v_fmac_f32 %0, %1, %6"
+      : "+v"(acc), "=&v"(t)
+      : "v"(w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+  return acc;
+}
+template <bool ASM>
+__device__ __forceinline__ float dot4u_(uint32_t w, const float* x, float acc) {
+  return ASM ? dot4u_asm(w, x, acc) : dot4u(w, x, acc);
+}
+template <bool ASM>
+__device__ __forceinline__ float dot4s_(uint32_t w, const float* x, float acc) {
+  return ASM ? dot4s_asm(w, x, acc) : dot4s(w, x, acc);
+}
+
 // One lane's 64-weight slice of one row: raw registers and the slice dot in
 // two halves of 32 weights.  voff(sl) is slice sl's byte offset in its row;
 // j = sl % 4 its quarter of a K-quant block.  dot(h, x, xs, j) takes half h's
@@ -69,13 +93,14 @@ template <> struct Slice<GQ_Q4_K> {           // sub-blocks 2j, 2j+1 of a super-
     q0 = bld16(r, vo + 32 * j, 16);
     q1 = bld16(r, vo + 32 * j, 32);
   }
+  template <bool ASM>
   __device__ float dot(int h, const float* x, const float* xs, int j) const {
     const u32x4 q = h ? q1 : q0;              // sub-block 2j + h
     float s = 0.f, t = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {             // low nibbles: elements 4k.., high: 16+4k..
-      s = dot4u(q[k] & 0x0F0F0F0Fu, x + 4 * k, s);
-      t = dot4u((q[k] >> 4) & 0x0F0F0F0Fu, x + 16 + 4 * k, t);
+      s = dot4u_<ASM>(q[k] & 0x0F0F0F0Fu, x + 4 * k, s);
+      t = dot4u_<ASM>((q[k] >> 4) & 0x0F0F0F0Fu, x + 16 + 4 * k, t);
     }
     // (scale, min) of sub-blocks 2j, 2j+1: the 24 bits at bit 24j of the
     // 96-bit field stream in header bytes 4..15
@@ -99,6 +124,7 @@ template <> struct Slice<GQ_Q6_K> {           // 32-weight groups 2j, 2j+1
     sc = bld4(r, vo + 4 * j, 2);
     d = bld2(r, vo, 0);
   }
+  template <bool ASM>
   __device__ float dot(int g, const float* x, const float* xs, int) const {
     // group 2j + g; unsigned codes q = low4 | high2 << 4; per 16-weight
     // quarter sum((q - 32) * x) = sum(q * x) - 32 * sum(x)
@@ -130,12 +156,13 @@ template <> struct Slice<GQ_Q8_0> {           // blocks 2*sl, 2*sl+1
     c[2] = bld16(r, vo, 36);
     c[3] = bld16(r, vo, 52);
   }
+  template <bool ASM>
   __device__ float dot(int h, const float* x, const float*, int) const {
     float a = 0.f, b = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {
-      a = dot4s(c[2 * h][k], x + 4 * k, a);
-      b = dot4s(c[2 * h + 1][k], x + 16 + 4 * k, b);
+      a = dot4s_<ASM>(c[2 * h][k], x + 4 * k, a);
+      b = dot4s_<ASM>(c[2 * h + 1][k], x + 16 + 4 * k, b);
     }
     return h2f(h ? d1 : d0) * (a + b);
   }
@@ -159,6 +186,7 @@ template <int T> struct SliceQ40Q50 {
     h0 = Q5 ? bld4(r, vo, 2) : 0u;
     h1 = Q5 ? bld4(r, vo, BB + 2) : 0u;
   }
+  template <bool ASM>
   __device__ float dot(int h, const float* x, const float*, int) const {
     const u32x4 q = h ? q1 : q0;
     const uint32_t qh = h ? h1 : h0;
@@ -170,8 +198,8 @@ template <int T> struct SliceQ40Q50 {
         lo |= spread4_bit4(qh >> (4 * k));
         hi |= spread4_bit4(qh >> (16 + 4 * k));
       }
-      a = dot4s(centre<OFF>(lo), x + 4 * k, a);
-      b = dot4s(centre<OFF>(hi), x + 16 + 4 * k, b);
+      a = dot4s_<ASM>(centre<OFF>(lo), x + 4 * k, a);
+      b = dot4s_<ASM>(centre<OFF>(hi), x + 16 + 4 * k, b);
     }
     return h2f(h ? d1 : d0) * (a + b);
   }
@@ -191,13 +219,24 @@ __device__ __forceinline__ int xswz(int f) {
 // (a wave holds 64/LPR rows side by side when rows are short); each wave takes
 // R such row sets per group and walks its groups pass by pass, so the double
 // buffer holds one pass whatever the row length.
-template <int T, bool XF16, int LPR, int R, int XPT, bool XFIRST>
+// Decode-layer fusions (template F): F_NORM stages RMSNorm(x) instead of x
+// (one more barrier, for the sum of squares); F_GLU reads a second matrix of
+// the same shape (row set 1 from blob2, the same rows as row set 0 from
+// blob) and stores silu(row set 0) * row set 1.
+constexpr int F_NORM = 1, F_GLU = 2;
+
+template <int T, bool XF16, int LPR, int R, int XPT, bool XFIRST, int F = 0>
 __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, int rows,
                                               int cols, int rb, const void* __restrict__ xv,
-                                              float* __restrict__ y) {
+                                              float* __restrict__ y,
+                                              const uint8_t* __restrict__ blob2 = nullptr,
+                                              const float* __restrict__ gamma = nullptr,
+                                              float eps = 0.f) {
   extern __shared__ float xsm[];           // x padded to whole slices, then 16-column sums
+  constexpr bool NORM = (F & F_NORM) != 0, GLU = (F & F_GLU) != 0;
+  static_assert(!GLU || R == 2, "the gated form takes two row sets");
   constexpr int RPW = 64 / LPR;            // rows side by side in a wave
-  constexpr int ROWS = RPW * R;            // rows per group
+  constexpr int ROWS = GLU ? RPW : RPW * R;   // rows per group
   // XPT = float4 of x staged per thread: cols <= XPT * 1024
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
@@ -212,7 +251,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   // x from global first (clamped, unconditional loads), then the first pass's
   // weights, then x into LDS: the LDS stores wait only for x
   const int nc4 = cols >> 2;
-  f32x4 xr[XPT];
+  f32x4 xr[XPT], gr[NORM ? XPT : 1];
 #pragma unroll
   for (int i = 0; i < XPT; i++) {
     const int cc = min((int)threadIdx.x + 256 * i, nc4 - 1);
@@ -222,6 +261,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
     } else {
       xr[i] = reinterpret_cast<const f32x4*>(xv)[cc];
     }
+    if constexpr (NORM) gr[i] = reinterpret_cast<const f32x4*>(gamma)[cc];
   }
 
   Slice<T> cur[R];
@@ -232,9 +272,10 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
     const int vo = Slice<T>::voff(sl);
 #pragma unroll
     for (int k = 0; k < R; k++) {
-      const int rw0 = uniform(grp * ROWS + k * RPW);
+      const int rw0 = uniform(grp * ROWS + (GLU ? 0 : k * RPW));
       const int nr = max(0, min(RPW, rows - rw0));
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(blob + (int64_t)rw0 * rb, (uint32_t)(nr * rb));
+      const uint8_t* const b = (GLU && k == 1) ? blob2 : blob;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(b + (int64_t)rw0 * rb, (uint32_t)(nr * rb));
       w[k].load(rs, sub * rb + vo, sl & 3);
     }
   };
@@ -254,9 +295,37 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   };
   if constexpr (!XFIRST) first_two();
 
+  // RMSNorm ("How LLM Inference Engines Work", "RMSNorm"): s = rsqrt(mean(x^2)
+  // + eps) in fp32, x' = (x * s rounded to x's type) * gamma.  Every
+  // workgroup forms the sum of squares itself: per thread, then the DPP
+  // network, then the four waves in order through LDS.
+  float* xsum = xsm + cpad;
+  if constexpr (NORM) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+      const int c4 = (int)threadIdx.x + 256 * i;
+      const f32x4 v = (c4 < nc4) ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      q += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
+    }
+    q = group_sum_dpp<64>(q);                // the wave's total in lane 63
+    float* const part = xsum + (cpad >> 4);  // 4 floats after the column sums
+    if (lane == 63) part[wave] = q;
+    __syncthreads();
+    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    const float sc = 1.f / sqrtf(tot / (float)cols + eps);
+#pragma unroll
+    for (int i = 0; i < XPT; i++) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        float t = xr[i][e] * sc;
+        if constexpr (XF16) t = (float)(_Float16)t;
+        xr[i][e] = t * gr[i][e];
+      }
+    }
+  }
   // x (fp32, zero-padded to whole slices) into LDS; each quad of lanes holds
   // one 16-column group, summed on the DPP network
-  float* xsum = xsm + cpad;
 #pragma unroll
   for (int i = 0; i < XPT; i++) {
     const int c4 = (int)threadIdx.x + 256 * i;
@@ -303,7 +372,8 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
         const bool use = live && (h == 0 || second);
 #pragma unroll
         for (int k = 0; k < R; k++) {
-          const float d = cur[k].dot(h, x, xs, s & 3);
+          // two row sets: convert + FMA pairs kept together (see dot4u_asm)
+          const float d = cur[k].template dot<(R > 1)>(h, x, xs, s & 3);
           acc[k] += use ? d : 0.f;
         }
       }
@@ -312,11 +382,19 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
         for (int k = 0; k < R; k++) cur[k] = nxt[k];
       }
     }
+    if constexpr (GLU) {
+      // SwiGLU ("How LLM Inference Engines Work", "SwiGLU Feed-Forward
+      // Network"): silu(gate) * up, silu(v) = v / (1 + exp(-v)), in fp32
+      const float gt = group_sum_dpp<LPR>(acc[0]), up = group_sum_dpp<LPR>(acc[1]);
+      const int r = g * ROWS + sub;
+      if (li == LPR - 1 && r < rows) y[r] = gt / (1.f + expf(-gt)) * up;
+    } else {
 #pragma unroll
-    for (int k = 0; k < R; k++) {
-      const float v = group_sum_dpp<LPR>(acc[k]);          // valid in lane LPR-1 of each group
-      const int r = g * ROWS + k * RPW + sub;
-      if (li == LPR - 1 && r < rows) y[r] = v;
+      for (int k = 0; k < R; k++) {
+        const float v = group_sum_dpp<LPR>(acc[k]);        // valid in lane LPR-1 of each group
+        const int r = g * ROWS + k * RPW + sub;
+        if (li == LPR - 1 && r < rows) y[r] = v;
+      }
     }
   }
 }
@@ -341,59 +419,90 @@ static int resident_wgs(K kern, size_t lds) {
   return cus * per;
 }
 
-template <int T, bool XF16, int LPR, int R, int XPT>
+// Fusion arguments of a decode-layer launch (all optional).
+struct Fuse {
+  const void* blob2;                       // up-projection weights: SwiGLU output
+  const float* gamma;                      // RMSNorm weights: x is normalized first
+  float eps;
+};
+
+template <int T, bool XF16, int LPR, int R, int XPT, int F>
 static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, const void* x,
-                              float* y, hipStream_t st) {
+                              float* y, const Fuse& fu, hipStream_t st) {
+  constexpr int RR = (F & F_GLU) ? 2 : R;
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t cpad = (cols + 63) / 64 * 64;
-  const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4;   // <= 68 KB for cols <= 16384
-  auto kern = k_gemv<T, XF16, LPR, R, XPT, false>;
+  // x, its 16-column sums and 4 per-wave partial sums: <= 68 KB for cols <= 16384
+  const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4 + 16;
+  auto kern = k_gemv<T, XF16, LPR, RR, XPT, false, F>;
   static size_t cap_lds = 0;               // resident workgroups for the last LDS size
   static int cap = 0;                      // (both orders use the same registers)
   if (cap_lds != lds) { cap = resident_wgs(kern, lds); cap_lds = lds; }
-  const int64_t groups = (rows + (64 / LPR) * R - 1) / ((64 / LPR) * R);
+  const int64_t rpg = (F & F_GLU) ? (64 / LPR) : (64 / LPR) * RR;   // rows per group
+  const int64_t groups = (rows + rpg - 1) / rpg;
   const int64_t wgs = (groups + 3) / 4;
   dim3 grid((unsigned)(wgs < cap ? wgs : cap));
   // items of the wave with the most: x goes first when that is at most 2
   const int64_t npass = ((cols + 63) / 64 + LPR - 1) / LPR;
   const int64_t most = (groups + 4 * (int64_t)grid.x - 1) / (4 * (int64_t)grid.x) * npass;
+  const uint8_t* b2 = (const uint8_t*)fu.blob2;
   if (most <= 2)
-    hipLaunchKernelGGL((k_gemv<T, XF16, LPR, R, XPT, true>), grid, dim3(256), lds, st,
-                       (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, y);
+    hipLaunchKernelGGL((k_gemv<T, XF16, LPR, RR, XPT, true, F>), grid, dim3(256), lds, st,
+                       (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, y, b2, fu.gamma,
+                       fu.eps);
   else
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t*)blob, (int)rows,
-                       (int)cols, (int)rb, x, y);
+                       (int)cols, (int)rb, x, y, b2, fu.gamma, fu.eps);
   return hipGetLastError();
 }
 
 // Shape dispatch: rows of up to 2048 weights share a wave (64/LPR of them);
 // longer rows take several passes of 64 slices.  Rows of up to 4096 weights
 // take R row sets per wave, longer ones one.
-template <int T, bool XF16>
+template <int T, bool XF16, int F>
 static hipError_t gemv_pick(const void* blob, int64_t rows, int64_t cols, const void* x, float* y,
-                            hipStream_t st) {
-  if (cols <= 1024) return gemv_launch<T, XF16, 16, GQ_GEMV_R, 4>(blob, rows, cols, x, y, st);
-  if (cols <= 2048) return gemv_launch<T, XF16, 32, GQ_GEMV_R, 4>(blob, rows, cols, x, y, st);
-  if (cols <= 4096) return gemv_launch<T, XF16, 64, GQ_GEMV_R, 4>(blob, rows, cols, x, y, st);
-  if (cols <= 8192) return gemv_launch<T, XF16, 64, 1, 8>(blob, rows, cols, x, y, st);
-  return gemv_launch<T, XF16, 64, 1, 16>(blob, rows, cols, x, y, st);
+                            const Fuse& fu, hipStream_t st) {
+  if (cols <= 1024) return gemv_launch<T, XF16, 16, GQ_GEMV_R, 4, F>(blob, rows, cols, x, y, fu, st);
+  if (cols <= 2048) return gemv_launch<T, XF16, 32, GQ_GEMV_R, 4, F>(blob, rows, cols, x, y, fu, st);
+  if (cols <= 4096) return gemv_launch<T, XF16, 64, GQ_GEMV_R, 4, F>(blob, rows, cols, x, y, fu, st);
+  if (cols <= 8192) return gemv_launch<T, XF16, 64, 1, 8, F>(blob, rows, cols, x, y, fu, st);
+  return gemv_launch<T, XF16, 64, 1, 16, F>(blob, rows, cols, x, y, fu, st);
+}
+
+template <int T, int F>
+static hipError_t gemv_f(const void* blob, int64_t rows, int64_t cols, const void* x, bool xf16,
+                         float* y, const Fuse& fu, hipStream_t st) {
+  return xf16 ? gemv_pick<T, true, F>(blob, rows, cols, x, y, fu, st)
+              : gemv_pick<T, false, F>(blob, rows, cols, x, y, fu, st);
 }
 
 template <int T>
 static hipError_t gemv_t(const void* blob, int64_t rows, int64_t cols, const void* x, bool xf16,
-                         float* y, hipStream_t st) {
-  return xf16 ? gemv_pick<T, true>(blob, rows, cols, x, y, st)
-              : gemv_pick<T, false>(blob, rows, cols, x, y, st);
+                         float* y, const Fuse& fu, hipStream_t st) {
+  const int f = (fu.gamma ? F_NORM : 0) | (fu.blob2 ? F_GLU : 0);
+  switch (f) {
+    case 0: return gemv_f<T, 0>(blob, rows, cols, x, xf16, y, fu, st);
+    case F_NORM: return gemv_f<T, F_NORM>(blob, rows, cols, x, xf16, y, fu, st);
+    case F_GLU: return gemv_f<T, F_GLU>(blob, rows, cols, x, xf16, y, fu, st);
+    default: return gemv_f<T, F_NORM | F_GLU>(blob, rows, cols, x, xf16, y, fu, st);
+  }
 }
 
 hipError_t launch_gemv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, hipStream_t st) {
+  return launch_gemv_fused(type, blob, nullptr, rows, cols, x, x_f16, nullptr, 0.f, y, st);
+}
+
+hipError_t launch_gemv_fused(int type, const void* blob, const void* up_blob, int64_t rows,
+                             int64_t cols, const void* x, bool x_f16, const float* norm_weight,
+                             float eps, float* y, hipStream_t st) {
+  const Fuse fu{up_blob, norm_weight, eps};
   switch (type) {
-    case GQ_Q4_0: return gemv_t<GQ_Q4_0>(blob, rows, cols, x, x_f16, y, st);
-    case GQ_Q5_0: return gemv_t<GQ_Q5_0>(blob, rows, cols, x, x_f16, y, st);
-    case GQ_Q8_0: return gemv_t<GQ_Q8_0>(blob, rows, cols, x, x_f16, y, st);
-    case GQ_Q4_K: return gemv_t<GQ_Q4_K>(blob, rows, cols, x, x_f16, y, st);
-    case GQ_Q6_K: return gemv_t<GQ_Q6_K>(blob, rows, cols, x, x_f16, y, st);
+    case GQ_Q4_0: return gemv_t<GQ_Q4_0>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q5_0: return gemv_t<GQ_Q5_0>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q8_0: return gemv_t<GQ_Q8_0>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q4_K: return gemv_t<GQ_Q4_K>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q6_K: return gemv_t<GQ_Q6_K>(blob, rows, cols, x, x_f16, y, fu, st);
   }
   return hipErrorInvalidValue;
 }

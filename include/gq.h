@@ -130,6 +130,30 @@ int gq_matmul_ex(const void *weight_blob, int ggml_type, int64_t rows, int64_t c
                  const void *x, int x_type, float *y, int64_t n_tok, void *stream);
 
 /*
+ * One decode token through a transformer sublayer's projection, with the
+ * steps on either side fused into the same launch:
+ *   xin = norm_weight ? RMSNorm(x) : x, where RMSNorm follows "How LLM
+ *         Inference Engines Work", section "RMSNorm": s = rsqrt(mean_c x[c]^2
+ *         + eps) in fp32, xin[c] = (x[c] * s, rounded to fp16 when x is fp16)
+ *         * norm_weight[c];
+ *   y   = up_blob ? silu(W^ xin) * (U^ xin) : W^ xin, elementwise over the
+ *         rows, silu(v) = v / (1 + exp(-v)) in fp32 (same page, "SwiGLU
+ *         Feed-Forward Network": the gate projection through SiLU times the
+ *         up projection).
+ *   weight_blob  device, rows*RB bytes (the gate weights when up_blob is set)
+ *   up_blob      device or NULL, a second blob of the same type and shape
+ *   x            device, one token: fp32 or fp16 [cols] (x_type), read only
+ *   norm_weight  device fp32 [cols] or NULL; eps >= 0 and finite
+ *   y            device, fp32 [rows], overwritten; must not overlap the inputs
+ * All pointers given are 16-byte aligned; cols <= 16384.  The sum of squares
+ * is formed in fp32 by every workgroup in a fixed order, so the result is the
+ * same on every run.  Errors as for gq_matmul_ex (a bad eps: GQ_EINVAL_SHAPE).
+ */
+int gq_matmul_decode(const void *weight_blob, const void *up_blob, int ggml_type, int64_t rows,
+                     int64_t cols, const void *x, int x_type, const float *norm_weight,
+                     float eps, float *y, void *stream);
+
+/*
  * Dequantize the whole blob into out[rows][cols] (device, 16-B aligned).
  *   out_type GQ_F32: bit-exact with the stated fp32 operation order: Q4_K
  *     forms a = d*sc and b = dmin*m in fp32 (exact) and rounds once in

@@ -76,6 +76,8 @@ class Oracle:
         lib.gqo_dequant_f32.argtypes = [ci, vp, i64, i64, vp]
         lib.gqo_dequant_f64.argtypes = [ci, vp, i64, i64, vp]
         lib.gqo_matmul_f64.argtypes = [ci, vp, i64, i64, vp, i64, vp, vp, ci]
+        lib.gqo_rmsnorm_f64.argtypes = [vp, i64, vp, ctypes.c_double, ci, vp]
+        lib.gqo_swiglu_f64.argtypes = [vp, vp, i64, vp]
         self.lib = lib
         self.plant = plant
 
@@ -152,6 +154,31 @@ class Oracle:
         return y, yabs
 
 
+    def rmsnorm_f64(self, x: np.ndarray, w: np.ndarray, eps: float, half_x: bool = False):
+        """RMSNorm of the vector x with weights w (fp64; see gqo.h)."""
+        x = np.ascontiguousarray(np.asarray(x).reshape(-1).astype(np.float64))
+        w = np.ascontiguousarray(np.asarray(w).reshape(-1).astype(np.float64))
+        if w.size != x.size:
+            raise ValueError("x and w differ in length")
+        out = np.empty_like(x)
+        rc = self.lib.gqo_rmsnorm_f64(_ptr(x), x.size, _ptr(w), float(eps), int(bool(half_x)), _ptr(out))
+        if rc:
+            raise ValueError(f"gqo_rmsnorm_f64 failed ({rc})")
+        return out
+
+    def swiglu_f64(self, g: np.ndarray, u: np.ndarray):
+        """silu(g) * u elementwise (fp64)."""
+        g = np.ascontiguousarray(np.asarray(g, dtype=np.float64))
+        u = np.ascontiguousarray(np.asarray(u, dtype=np.float64))
+        if g.shape != u.shape:
+            raise ValueError("g and u differ in shape")
+        out = np.empty_like(g)
+        rc = self.lib.gqo_swiglu_f64(_ptr(g), _ptr(u), g.size, _ptr(out))
+        if rc:
+            raise ValueError(f"gqo_swiglu_f64 failed ({rc})")
+        return out
+
+
 _default = None
 
 
@@ -196,3 +223,11 @@ def dequant_f64(blob, t, rows, cols):
 
 def matmul_f64(blob, t, rows, cols, x, threads=1):
     return _load().matmul_f64(blob, t, rows, cols, x, threads)
+
+
+def rmsnorm_f64(x, w, eps, half_x=False):
+    return _load().rmsnorm_f64(x, w, eps, half_x)
+
+
+def swiglu_f64(g, u):
+    return _load().swiglu_f64(g, u)

@@ -18,6 +18,10 @@
  *  [LK]  "Local LLM inference (experimental, --features llm)", section
  *        "The mmap backend" (Q4_K_M mixes Q4_K, Q5_0, Q6_K, Q8_0, F32 and
  *        dequantizes every block inside the dot product).
+ *  [NL]  also sections "RMSNorm" (scale by the reciprocal root of the mean
+ *        square plus eps, computed in float32, the product cast back to the
+ *        input's type, then times the weight) and "SwiGLU Feed-Forward
+ *        Network" (SiLU of the gate projection times the up projection).
  *
  * Readings where the pages are silent (each one is listed in the design notes):
  *  R1 Q4_K 6-bit fields: one 96-bit little-endian stream, field k at bits
@@ -49,7 +53,8 @@
  * builds that check the pins reject it; the normal build uses 0:
  *   1 nibble order swapped, 2 Q4_K min added instead of subtracted,
  *   3 Q4_K scale/min fields swapped, 4 Q6_K offset 31 instead of 32,
- *   5 dot drops the last column, 6 dot reads x transposed. */
+ *   5 dot drops the last column, 6 dot reads x transposed,
+ *   7 RMSNorm leaves out eps, 8 SiLU uses exp(+v). */
 #ifndef GQO_PLANT
 #define GQO_PLANT 0
 #endif
@@ -324,6 +329,35 @@ int gqo_matmul_f64(int type, const uint8_t *blob, int64_t rows, int64_t cols,
             if (yabs) yabs[t * rows + r] = sa;
         }
         free(w);
+    }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- decode-layer steps [NL] */
+
+int gqo_rmsnorm_f64(const double *x, int64_t cols, const double *w, double eps, int half_x,
+                    double *out) {
+    if (!x || !w || !out) return -3;
+    if (cols < 1 || !(eps >= 0.0)) return -2;
+    double ss = 0.0;
+    for (int64_t c = 0; c < cols; c++) ss += x[c] * x[c];
+    const double mean = ss / (double)cols;
+    const double s = 1.0 / sqrt((GQO_PLANT == 7) ? mean : mean + eps);
+    for (int64_t c = 0; c < cols; c++) {
+        double t = x[c] * s;
+        if (half_x) t = gqo_half_to_double(gqo_half_rne((float)t));   /* cast back to fp16 x */
+        out[c] = t * w[c];
+    }
+    return 0;
+}
+
+int gqo_swiglu_f64(const double *g, const double *u, int64_t n, double *out) {
+    if (!g || !u || !out) return -3;
+    if (n < 0) return -2;
+    for (int64_t i = 0; i < n; i++) {
+        const double v = g[i];
+        const double silu = v / (1.0 + exp((GQO_PLANT == 8) ? v : -v));
+        out[i] = silu * u[i];
     }
     return 0;
 }

@@ -46,6 +46,19 @@ int gqo_dequant_f64(int type, const uint8_t *blob, int64_t rows, int64_t cols, d
 int gqo_matmul_f64(int type, const uint8_t *blob, int64_t rows, int64_t cols,
                    const double *x, int64_t n_tok, double *y, double *yabs, int threads);
 
+/*
+ * RMSNorm of one vector ("How LLM Inference Engines Work", "RMSNorm"):
+ * s = 1/sqrt(mean_c x[c]^2 + eps), out[c] = (x[c]*s) * w[c] in fp64, except
+ * that with half_x the product x[c]*s is first rounded to fp16 (through fp32),
+ * as the page casts it back to an fp16 input's type.
+ */
+int gqo_rmsnorm_f64(const double *x, int64_t cols, const double *w, double eps, int half_x,
+                    double *out);
+
+/* SwiGLU output (same page, "SwiGLU Feed-Forward Network"):
+ * out[i] = silu(g[i]) * u[i], silu(v) = v / (1 + exp(-v)), in fp64. */
+int gqo_swiglu_f64(const double *g, const double *u, int64_t n, double *out);
+
 #ifdef __cplusplus
 }
 #endif

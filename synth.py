@@ -41,6 +41,13 @@ def activations(n_tok: int, cols: int, seed: int, dtype: str = "f32") -> np.ndar
     return x
 
 
+def norm_weights(cols: int, seed: int) -> np.ndarray:
+    """fp32 [cols] ~ N(1, 0.1^2): RMSNorm weights of a trained layer sit
+    near one (the page's module initializes them to ones)."""
+    rng = np.random.default_rng(seed)
+    return (1.0 + 0.1 * rng.standard_normal(cols)).astype(np.float32)
+
+
 def random_bytes(n: int, seed: int) -> np.ndarray:
     """Uniform random bytes (fuzz blobs: every bit pattern, NaN/Inf scales too)."""
     return np.random.default_rng(seed).integers(0, 256, size=n, dtype=np.uint8)

@@ -14,7 +14,8 @@ What each pin rests on:
     int64), Q4_K with constant codes per sub-block reduces to per-sub-block sums;
   * invariants: power-of-two scaling is exact, row permutation permutes y,
     n tokens in one call equal n calls;
-  * the quantizer's round-trip error bound derived from its definition.
+  * the quantizer's round-trip error bound derived from its definition;
+  * RMSNorm and SiLU: closed forms, identities and invariants.
 """
 from __future__ import annotations
 
@@ -234,5 +235,52 @@ def pin_roundtrip(o):
             assert np.all(err <= _roundtrip_bound(w, t) * (1 + 1e-9) + 1e-12), t
 
 
+def pin_rmsnorm(o):
+    """RMSNorm ("How LLM Inference Engines Work", "RMSNorm") against closed
+    forms and invariants: x = (3, 4) has mean square 12.5, so eps = 3.5 gives
+    the scale 1/sqrt(16) = 1/4 exactly; a constant vector with eps = 0
+    normalizes to its sign; with eps = 0 a positive rescaling of x changes
+    nothing and the output's mean square (unit weights) is 1; the weights
+    multiply elementwise; fp16 inputs round x*s to binary16 (NumPy's) first."""
+    out = o.rmsnorm_f64(np.array([3.0, 4.0]), np.array([1.0, 2.0]), 3.5)
+    assert np.array_equal(out, np.array([0.75, 2.0])), out
+    out = o.rmsnorm_f64(np.full(7, -2.5), np.ones(7), 0.0)
+    assert np.array_equal(out, np.full(7, -1.0)), out
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(4096)
+    w = rng.standard_normal(4096)
+    a = o.rmsnorm_f64(x, np.ones(4096), 0.0)
+    assert abs(np.mean(a * a) - 1.0) < 1e-12
+    b = o.rmsnorm_f64(x * 37.0, np.ones(4096), 0.0)
+    assert np.allclose(a, b, rtol=1e-13, atol=0)
+    c = o.rmsnorm_f64(x, w, 1e-5)
+    assert np.allclose(c, o.rmsnorm_f64(x, np.ones(4096), 1e-5) * w, rtol=1e-15, atol=0)
+    # eps enters as mean + eps: x = 0 stays 0 (and finite) for eps > 0
+    assert np.array_equal(o.rmsnorm_f64(np.zeros(5), np.ones(5), 1e-6), np.zeros(5))
+    xh = rng.standard_normal(1000).astype(np.float16).astype(np.float64)
+    s = 1.0 / np.sqrt(np.mean(xh * xh) + 1e-5)
+    got = o.rmsnorm_f64(xh, np.ones(1000), 1e-5, half_x=True)
+    ref = (xh * s).astype(np.float32).astype(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref), int(np.sum(got != ref))
+
+
+def pin_swiglu(o):
+    """SiLU ("SwiGLU Feed-Forward Network") against identities and closed
+    forms: silu(0) = 0; silu(v) - silu(-v) = v (sigmoid(v) + sigmoid(-v) = 1);
+    sigmoid(ln 3) = 3/4 so silu(ln 3) = (3/4) ln 3; silu(v) ~ v for large v and
+    ~ 0 for very negative v; the up projection multiplies elementwise."""
+    v = np.linspace(-30, 30, 601)
+    one = np.ones_like(v)
+    sp, sn = o.swiglu_f64(v, one), o.swiglu_f64(-v, one)
+    assert np.allclose(sp - sn, v, rtol=0, atol=1e-12)
+    assert o.swiglu_f64(np.array([0.0]), np.array([5.0]))[0] == 0.0
+    l3 = np.log(3.0)
+    assert abs(o.swiglu_f64(np.array([l3]), np.array([1.0]))[0] - 0.75 * l3) < 1e-15
+    assert abs(o.swiglu_f64(np.array([50.0]), np.array([1.0]))[0] - 50.0) < 1e-12
+    assert abs(o.swiglu_f64(np.array([-50.0]), np.array([1.0]))[0]) < 1e-18
+    u = np.linspace(-2, 3, 601)
+    assert np.allclose(o.swiglu_f64(v, u), sp * u, rtol=1e-15, atol=0)
+
+
 ALL_PINS = [pin_golden, pin_sizes, pin_fraction_dot, pin_q8_integer, pin_q4k_structured,
-            pin_pow2_and_perm, pin_f32_is_one_rounding, pin_roundtrip]
+            pin_pow2_and_perm, pin_f32_is_one_rounding, pin_roundtrip, pin_rmsnorm, pin_swiglu]

@@ -10,8 +10,8 @@ import oracle
 
 def test_exports_every_declared_symbol():
     names = gq.header_symbols()
-    assert {"gq_matmul", "gq_matmul_ex", "gq_dequant", "gq_quantize", "gq_type_info",
-            "gq_row_bytes", "gq_strerror"} <= set(names)
+    assert {"gq_matmul", "gq_matmul_ex", "gq_matmul_decode", "gq_dequant", "gq_quantize",
+            "gq_type_info", "gq_row_bytes", "gq_strerror"} <= set(names)
     L = gq.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -75,3 +75,29 @@ def test_dequant_and_quantize_validation():
     assert L.gq_quantize(A, gq.Q4_K, 4, 200, B, None) == -2
     assert L.gq_quantize(None, gq.Q4_K, 4, 256, B, None) == -3
     assert L.gq_quantize(A, gq.Q4_K, 4, 256, A + 64, None) == -3
+
+
+C = 0x30000
+N = 0x40000          # fake norm weights
+U = 0x50000          # fake up-projection blob
+
+
+@pytest.mark.parametrize("args,code", [
+    ((A, None, 99, 16, 256, B, gq.F32, None, 1e-5, C, None), -1),      # bad type
+    ((A, None, gq.Q4_K, 16, 256, B, gq.Q8_0, None, 1e-5, C, None), -1),  # bad x_type
+    ((A, None, gq.Q4_K, 16, 100, B, gq.F32, None, 1e-5, C, None), -2),   # cols % 256
+    ((A, None, gq.Q4_K, 16, 256, B, gq.F32, N, -1.0, C, None), -2),      # eps < 0
+    ((A, None, gq.Q4_K, 16, 256, B, gq.F32, N, float("nan"), C, None), -2),   # eps NaN
+    ((A, None, gq.Q4_K, 16, 256, B, gq.F32, N, float("inf"), C, None), -2),   # eps inf
+    ((None, U, gq.Q4_K, 16, 256, B, gq.F32, N, 1e-5, C, None), -3),      # null blob
+    ((A, U, gq.Q4_K, 16, 256, None, gq.F32, N, 1e-5, C, None), -3),      # null x
+    ((A, U, gq.Q4_K, 16, 256, B, gq.F32, N, 1e-5, None, None), -3),      # null y
+    ((A, U + 4, gq.Q4_K, 16, 256, B, gq.F32, N, 1e-5, C, None), -4),     # misaligned up blob
+    ((A, U, gq.Q4_K, 16, 256, B, gq.F32, N + 8, 1e-5, C, None), -4),     # misaligned norm weights
+    ((A, U, gq.Q4_K, 16, 256, B, gq.F32, N, 1e-5, N + 16, None), -3),    # y overlaps norm weights
+    ((A, U, gq.Q4_K, 16, 256, B, gq.F32, N, 1e-5, U + 32, None), -3),    # y overlaps up blob
+    ((A, U, gq.Q4_K, 16, 256, B, gq.F32, N, 1e-5, B + 16, None), -3),    # y overlaps x
+    ((A, U, gq.Q4_K, 16, 32768, B, gq.F32, N, 1e-5, C, None), -5),       # cols beyond the LDS limit
+])
+def test_matmul_decode_validation(args, code):
+    assert gq.lib().gq_matmul_decode(*args) == code

@@ -222,6 +222,79 @@ def test_gemm_partial_wave_full_size(t, rows, cols, n):
     check_matmul(y0, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n}")
 
 
+# ---------------------------------------------------------------- decode-layer fusions
+
+def decode_reference(blob, up, t, rows, cols, x, xdt, nw, eps):
+    """(y_ref, tolerance) for gq_matmul_decode from the oracle: RMSNorm of x
+    (when nw is given), then W^ x or silu(W^ x) * (U^ x).  The gated form's
+    bound carries the matmul bar through h = silu(g) u: |silu'| <= 1.1, so
+    |dh| <= 1.1 |dg| (|u| + |du|) + |silu(g)| |du| with |dg|, |du| within
+    1e-3 of sum |w x|, plus a few fp32 roundings of h."""
+    xin = x.astype(np.float64).reshape(-1)
+    if nw is not None:
+        xin = oracle.rmsnorm_f64(xin, nw, eps, half_x=(xdt == "f16"))
+    g, ga = oracle.matmul_f64(blob, t, rows, cols, xin[None, :], threads=THREADS)
+    g, ga = g[0], ga[0]
+    if up is None:
+        return g, TOL * ga
+    u, ua = oracle.matmul_f64(up, t, rows, cols, xin[None, :], threads=THREADS)
+    u, ua = u[0], ua[0]
+    h = oracle.swiglu_f64(g, u)
+    sg = np.abs(oracle.swiglu_f64(g, np.ones_like(g)))
+    tol = 1.1 * TOL * ga * (np.abs(u) + TOL * ua) + TOL * sg * ua + 1e-6 * np.abs(h)
+    return h, tol
+
+
+DECODE_SHAPES = [("q4_k", 300, 4096), ("q6_k", 96, 11008), ("q8_0", 300, 352),
+                 ("q5_0", 75, 288), ("q4_0", 130, 2048), ("q4_k", 200, 768)]
+
+
+@pytest.mark.parametrize("t,rows,cols", DECODE_SHAPES)
+@pytest.mark.parametrize("xdt", ["f32", "f16"])
+def test_decode_fused(t, rows, cols, xdt):
+    """RMSNorm prologue and SwiGLU epilogue of gq_matmul_decode against the
+    oracle, in every combination; with neither, the call is bit-identical to
+    gq_matmul_ex at one token."""
+    _, blob = quantized(t, rows, cols, seed=121)
+    _, upb = quantized(t, rows, cols, seed=122)
+    bd, ud = to_dev(blob), to_dev(upb)
+    x = synth.activations(1, cols, seed=123, dtype=xdt)[0]
+    nw = synth.norm_weights(cols, seed=124)
+    xd, nd = to_dev(x), to_dev(nw)
+    plain = gq.matmul(bd, t, rows, cols, xd).cpu().numpy()[0]
+    none = gq.matmul_decode(bd, t, rows, cols, xd).cpu().numpy()
+    assert np.array_equal(plain.view(np.uint32), none.view(np.uint32))
+    for norm in (False, True):
+        for glu in (False, True):
+            if not (norm or glu):
+                continue
+            say(f"decode {t} {rows}x{cols} x={xdt} norm={norm} glu={glu}")
+            y = gq.matmul_decode(bd, t, rows, cols, xd, up=ud if glu else None,
+                                 norm_weight=nd if norm else None, eps=1e-5).cpu().numpy()
+            ref, tol = decode_reference(blob, upb if glu else None, t, rows, cols, x, xdt,
+                                        nw if norm else None, 1e-5)
+            err = np.abs(y.astype(np.float64) - ref)
+            say(f"  max err / tol = {float(np.max(err / np.maximum(tol, 1e-300))):.3e}")
+            assert np.all(err <= tol), (norm, glu, int(np.sum(err > tol)))
+
+
+def test_decode_fused_deterministic_and_scale_free():
+    """The normalized path repeats bit for bit, and RMSNorm makes the result
+    independent of a power-of-two scaling of x (exact in fp32 and fp16)."""
+    t, rows, cols = "q4_k", 512, 4096
+    _, blob = quantized(t, rows, cols, seed=125)
+    _, upb = quantized(t, rows, cols, seed=126)
+    bd, ud = to_dev(blob), to_dev(upb)
+    x = synth.activations(1, cols, seed=127)[0]
+    nw = to_dev(synth.norm_weights(cols, seed=128))
+    a = gq.matmul_decode(bd, t, rows, cols, to_dev(x), up=ud, norm_weight=nw, eps=0.0).cpu().numpy()
+    b = gq.matmul_decode(bd, t, rows, cols, to_dev(x), up=ud, norm_weight=nw, eps=0.0).cpu().numpy()
+    c = gq.matmul_decode(bd, t, rows, cols, to_dev(x * np.float32(8.0)), up=ud, norm_weight=nw,
+                         eps=0.0).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.array_equal(a.view(np.uint32), c.view(np.uint32))
+
+
 # ---------------------------------------------------------------- exact special cases
 
 def _q8_unit_blob(codes):
