@@ -20,6 +20,8 @@ Method:
     rotating over >= 512 MB of copies; achieved = blob bytes per launch /
     average launch duration, against the 8 TB/s HBM peak; traffic from the
     committed counter summary when it was taken on the current kernel source;
+  * fused_layer: the same step with the RMSNorm and SwiGLU fusions of the
+    decode entry point on (same weight bytes; norm and gate work added);
   * secondary: the Q4_K 11008x4096 dequant-GEMM at 512 fp16 tokens (GFLOP/s
     against the 2.5 PFLOP/s dense fp16 matrix peak) and a sweep of the other
     workload shapes;
@@ -261,6 +263,43 @@ def sweep(steps):
     return out
 
 
+def fused_layer(mats, steps, warmup):
+    """The same layer with the decode fusions on, as an engine would run it:
+    RMSNorm fused ahead of qkv, attn_o plain, RMSNorm fused ahead of the
+    gate and up halves with the SwiGLU product written by that launch, and
+    ffn_down reading that product.  Same weight bytes as the plain step,
+    three fewer launches than an engine that normalises and gates apart."""
+    import torch
+    import gguf_quant_matmul_amd as gq
+    import synth
+    by = {m.name: m for m in mats}
+    qkv, o, gu, down = by["qkv"], by["attn_o"], by["ffn_gate_up"], by["ffn_down"]
+    lib = gq.lib()
+    half = gu.bytes // 2
+    nw1 = torch.from_numpy(synth.norm_weights(qkv.cols, seed=7900)).cuda()
+    nw2 = torch.from_numpy(synth.norm_weights(gu.cols, seed=7901)).cuda()
+    h = torch.empty(gu.rows // 2, dtype=torch.float32, device="cuda")
+    ncopy = len(qkv.copies)
+
+    def call(blob, up, m, rows, x, xt, nw, y, sp):
+        rc = lib.gq_matmul_decode(blob, up, m.tid, rows, m.cols, x, xt, nw, ctypes.c_float(1e-5), y, sp)
+        if rc:
+            raise RuntimeError(f"gq_matmul_decode({m.name}) failed: {gq.strerror(rc)}")
+
+    graphs = []
+    for ci in range(ncopy):
+        def fn(sp, ci=ci):
+            call(qkv.copies[ci].data_ptr(), None, qkv, qkv.rows, qkv.x.data_ptr(), qkv.xt,
+                 nw1.data_ptr(), qkv.y.data_ptr(), sp)
+            o.launch(ci, sp)
+            g = gu.copies[ci].data_ptr()
+            call(g, g + half, gu, gu.rows // 2, gu.x.data_ptr(), gu.xt, nw2.data_ptr(), h.data_ptr(), sp)
+            call(down.copies[ci].data_ptr(), None, down, down.rows, h.data_ptr(), gq.F32,
+                 None, down.y.data_ptr(), sp)
+        graphs.append(capture(fn))
+    return time_graphs(graphs, steps, warmup)
+
+
 def profile_launches(mats, n):
     """Plain launches for rocprofv3, in dispatch order: each layer matrix n
     times in turn (rotating copies), then n single-dispatch elementwise
@@ -326,6 +365,14 @@ def main():
     ms = time_graphs(step_graphs, args.steps, args.warmup)
     value = layer_bytes / (ms * 1e-3) / 1e9
 
+    log("timing the fused layer step")
+    fms = fused_layer(mats, args.steps, args.warmup)
+    fused = {"what": "same layer, RMSNorm fused ahead of qkv and gate/up, SwiGLU product "
+                     "written by the gate/up launch, ffn_down reading it (4 launches)",
+             "ms_per_step": round(fms, 5), "GBps": round(layer_bytes / (fms * 1e-3) / 1e9, 1),
+             "vs_plain_step": round(ms / fms, 4)}
+    log(f"  fused layer: {fms*1e3:.2f} us/step ({fused['GBps']} GB/s); plain {ms*1e3:.2f} us")
+
     # per-kernel live timing; a kernel is a (type, launch shape) instantiation
     per, kernels = [], {}
     for m in mats:
@@ -380,6 +427,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "fused_layer": fused,
         "per_launch": per,
         "sweep": shapes,
     }
