@@ -158,7 +158,53 @@ def time_graphs(graphs, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def kernel_time_ms(mat, steps, per_graph=16):
+def replay_spread(graphs, n, per_graph):
+    """p10 / p50 / p90 of the per-launch time (ms) over n individually timed
+    replays of graphs holding per_graph launches each."""
+    import torch
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        graphs[i % len(graphs)].replay()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev]) / per_graph
+    return [float(np.percentile(t, q)) for q in (10, 50, 90)]
+
+
+def stream_read_reference(steps):
+    """Achieved bandwidth of the library's plain streaming-read kernel
+    (gq_probe_stream_read: 128-bit loads, every byte once) at the dominant
+    launch's size and at 1 GiB, rotating over copies totalling >= 2x the
+    Infinity Cache: the practical ceiling the GEMV's fraction of the nominal
+    peak is read against."""
+    import torch
+    import gguf_quant_matmul_amd as gq
+    out = {}
+    for label, nbytes in (("29.5 MB", 29491200), ("1 GiB", 1 << 30)):
+        k = max(2, -(-2 * CACHE_BYTES // nbytes))
+        bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device="cuda") for i in range(k)]
+        res = torch.empty(gq.PROBE_OUT_WORDS, dtype=torch.int32, device="cuda")
+        per = 16 if nbytes < (64 << 20) else 2
+        graphs = []
+        for gi in range(-(-k // per)):
+            def fn(sp, gi=gi):
+                for j in range(per):
+                    rc = gq.lib().gq_probe_stream_read(bufs[(gi * per + j) % k].data_ptr(), nbytes,
+                                                       res.data_ptr(), sp)
+                    if rc:
+                        raise RuntimeError(f"gq_probe_stream_read: {gq.strerror(rc)}")
+            graphs.append(capture(fn))
+        ms = time_graphs(graphs, max(16, steps // per), warmup=2) / per
+        out[label] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        del bufs, graphs
+        torch.cuda.empty_cache()
+    return {"kernel": "gq_probe_stream_read (128-bit loads, each byte once)", "GBps": out}
+
+
+def kernel_time_ms(mat, steps, per_graph=16, spread=False):
     """Live HIP-event timing of back-to-back launches of one matrix, rotating
     over copies totalling >= 2x the Infinity Cache."""
     mat.ensure_copies(2 * CACHE_BYTES)
@@ -169,6 +215,8 @@ def kernel_time_ms(mat, steps, per_graph=16):
                 mat.launch(gi * per_graph + j, sp)
         graphs.append(capture(fn))
     ms = time_graphs(graphs, max(4, steps // per_graph), warmup=2)
+    if spread:
+        return ms / per_graph, replay_spread(graphs, 32, per_graph)
     return ms / per_graph
 
 
@@ -376,9 +424,10 @@ def main():
     # per-kernel live timing; a kernel is a (type, launch shape) instantiation
     per, kernels = [], {}
     for m in mats:
-        kms = kernel_time_ms(m, args.steps)
+        kms, (p10, p50, p90) = kernel_time_ms(m, args.steps, spread=True)
         per.append({"launch": m.name, "type": m.t, "rows": m.rows, "cols": m.cols,
                     "blob_bytes": m.bytes, "us_per_launch": round(kms * 1e3, 3),
+                    "us_p10_p50_p90": [round(p10 * 1e3, 3), round(p50 * 1e3, 3), round(p90 * 1e3, 3)],
                     "GBps": round(m.bytes / (kms * 1e-3) / 1e9, 1)})
         log(f"  {m.name:12s} {m.t} {m.rows}x{m.cols}: {kms*1e3:.2f} us  {per[-1]['GBps']} GB/s")
         key = f"gemv {m.t}, {m.cols} cols, fp32 x, batch 1"
@@ -396,6 +445,10 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": dom_key, "launches_per_step": dom["launches"],
                 "bytes_per_launch": avg_bytes, "us_per_launch": round(avg_us, 3)}
+
+    log("streaming-read reference")
+    roofline["stream_read_reference"] = stream_read_reference(args.steps)
+    log(f"  {roofline['stream_read_reference']}")
 
     secondary, shapes = None, None
     if not args.no_sweep:

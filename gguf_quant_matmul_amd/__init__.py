@@ -50,6 +50,8 @@ def lib():
         L.gq_matmul_ex.restype = ci
         L.gq_matmul_decode.argtypes = [vp, vp, ci, i64, i64, vp, ci, vp, ctypes.c_float, vp, vp]
         L.gq_matmul_decode.restype = ci
+        L.gq_probe_stream_read.argtypes = [vp, i64, vp, vp]
+        L.gq_probe_stream_read.restype = ci
         L.gq_dequant.argtypes = [vp, ci, i64, i64, vp, ci, vp]
         L.gq_dequant.restype = ci
         L.gq_quantize.argtypes = [vp, ci, i64, i64, vp, vp]
@@ -139,6 +141,24 @@ def matmul_decode(blob, t, rows: int, cols: int, x, up=None, norm_weight=None, e
                                 float(eps), out.data_ptr(), _stream(stream))
     if rc:
         raise GQError(rc, "gq_matmul_decode")
+    return out
+
+
+PROBE_OUT_WORDS = 2048
+
+
+def probe_stream_read(buf, out=None, stream=None):
+    """Streaming read of a contiguous CUDA tensor's bytes (the measured
+    bandwidth ceiling); returns the int32 tensor of per-workgroup XORs."""
+    import torch
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if out is None:
+        out = torch.empty(PROBE_OUT_WORDS, dtype=torch.int32, device=buf.device)
+    rc = lib().gq_probe_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(),
+                                    out.data_ptr(), _stream(stream))
+    if rc:
+        raise GQError(rc, "gq_probe_stream_read")
     return out
 
 

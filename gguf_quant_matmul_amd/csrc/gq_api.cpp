@@ -140,6 +140,15 @@ int gq_matmul_decode(const void* weight_blob, const void* up_blob, int ggml_type
                                           (hipStream_t)stream));
 }
 
+int gq_probe_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  if (bytes < 0 || bytes % 16) return GQ_EINVAL_SHAPE;
+  if (bytes > ((int64_t)1 << 30)) return GQ_EOVERFLOW;
+  if (!out || (bytes > 0 && !buf)) return GQ_EINVAL_PTR;
+  if (!aligned16(buf) || !aligned16(out)) return GQ_EALIGN;
+  if (overlap(buf, bytes, out, GQ_PROBE_OUT_WORDS * 4)) return GQ_EINVAL_PTR;
+  return hip_status(gq::launch_stream_read(buf, bytes, out, (hipStream_t)stream));
+}
+
 int gq_dequant(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols, void* out,
                int out_type, void* stream) {
   int64_t rb = 0;

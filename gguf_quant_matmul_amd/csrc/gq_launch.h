@@ -18,6 +18,9 @@ hipError_t launch_gemv(int type, const void* blob, int64_t rows, int64_t cols, c
 hipError_t launch_gemv_fused(int type, const void* blob, const void* up_blob, int64_t rows,
                              int64_t cols, const void* x, bool x_f16, const float* norm_weight,
                              float eps, float* y, hipStream_t st);
+// Streaming read of bytes (<= 2^30, a multiple of 16) into per-workgroup
+// XORs, GQ_PROBE_OUT_WORDS of them.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t st);
 // Small batches: the weight stream on the matrix cores, 16 tokens per pass.
 hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                       bool x_f16, float* y, int64_t n_tok, hipStream_t st);

@@ -176,6 +176,22 @@ int gq_dequant(const void *weight_blob, int ggml_type, int64_t rows, int64_t col
 int gq_quantize(const float *w, int ggml_type, int64_t rows, int64_t cols,
                 void *weight_blob, void *stream);
 
+/*
+ * Measurement: a plain streaming read of `bytes` bytes of device memory at
+ * buf with 128-bit loads, every byte read once, nothing else done.  Its
+ * bandwidth is the practical ceiling the GEMV kernels' effective bandwidth
+ * is read against (no kernel reaches the nominal HBM peak).  So that the
+ * reads cannot be dropped, out (device, GQ_PROBE_OUT_WORDS 32-bit words,
+ * overwritten) receives per-workgroup XORs of the buffer's 32-bit words:
+ * the XOR of all of out equals the XOR of all of buf's words.
+ *   buf    device, 16-byte aligned; bytes a multiple of 16, at most 2^30
+ *          (GQ_EINVAL_SHAPE / GQ_EOVERFLOW otherwise); with bytes = 0 buf
+ *          may be NULL and out is all zeros
+ *   out    device, 16-byte aligned, must not overlap buf
+ */
+#define GQ_PROBE_OUT_WORDS 2048
+int gq_probe_stream_read(const void *buf, int64_t bytes, uint32_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -101,3 +101,15 @@ U = 0x50000          # fake up-projection blob
 ])
 def test_matmul_decode_validation(args, code):
     assert gq.lib().gq_matmul_decode(*args) == code
+
+
+def test_probe_validation():
+    L = gq.lib()
+    assert L.gq_probe_stream_read(A, 100, B, None) == -2           # not a multiple of 16
+    assert L.gq_probe_stream_read(A, -16, B, None) == -2
+    assert L.gq_probe_stream_read(A, (1 << 30) + 16, B, None) == -5
+    assert L.gq_probe_stream_read(None, 64, B, None) == -3
+    assert L.gq_probe_stream_read(None, 0, None, None) == -3
+    assert L.gq_probe_stream_read(A, 64, None, None) == -3
+    assert L.gq_probe_stream_read(A + 8, 64, B, None) == -4
+    assert L.gq_probe_stream_read(A, 64, A + 32, None) == -3       # out overlaps buf

@@ -403,3 +403,17 @@ def test_zero_tokens_and_tiny():
     x1 = synth.activations(1, 256, seed=81)
     y = gq.matmul(bd, t, 1, 256, to_dev(x1)).cpu().numpy()
     check_matmul(y, blob, t, 1, 256, x1, label="1x256")
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 16 * 1000 + 16, 29491200, 40 << 20])
+def test_probe_stream_read_reads_every_word(nbytes):
+    """The streaming-read probe (the measured bandwidth ceiling) reads every
+    byte: the XOR of its per-workgroup outputs equals the buffer's."""
+    say(f"probe {nbytes} bytes")
+    host = synth.random_bytes(nbytes, seed=nbytes + 5)
+    buf = to_dev(host) if nbytes else torch.empty(0, dtype=torch.uint8, device=dev())
+    out = gq.probe_stream_read(buf)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    want = np.bitwise_xor.reduce(host.view(np.uint32)) if nbytes else np.uint32(0)
+    assert got == want
