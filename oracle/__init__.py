@@ -78,6 +78,7 @@ class Oracle:
         lib.gqo_matmul_f64.argtypes = [ci, vp, i64, i64, vp, i64, vp, vp, ci]
         lib.gqo_rmsnorm_f64.argtypes = [vp, i64, vp, ctypes.c_double, ci, vp]
         lib.gqo_swiglu_f64.argtypes = [vp, vp, i64, vp]
+        lib.gqo_attn_decode_f64.argtypes = [ci, vp, vp, i64, i64, i64, vp, i64, vp]
         self.lib = lib
         self.plant = plant
 
@@ -179,6 +180,25 @@ class Oracle:
         return out
 
 
+    def attn_decode_f64(self, k_cache: np.ndarray, v_cache: np.ndarray, t, kv_len: int,
+                        n_kv: int, head_dim: int, q: np.ndarray) -> np.ndarray:
+        """Decode-step GQA attention over quantized K/V caches (fp64; see gqo.h).
+        q: [n_heads][head_dim]; returns [n_heads][head_dim]."""
+        q = np.ascontiguousarray(np.asarray(q, dtype=np.float64))
+        n_heads = q.shape[0]
+        rb = self.row_bytes(t, head_dim)
+        for c in (k_cache, v_cache):
+            if c.size != kv_len * n_kv * rb:
+                raise ValueError("cache size does not match kv_len * n_kv rows")
+        out = np.empty((n_heads, head_dim), dtype=np.float64)
+        rc = self.lib.gqo_attn_decode_f64(_tid(t), _ptr(np.ascontiguousarray(k_cache)),
+                                          _ptr(np.ascontiguousarray(v_cache)), kv_len, n_kv,
+                                          head_dim, _ptr(q), n_heads, _ptr(out))
+        if rc:
+            raise ValueError(f"gqo_attn_decode_f64 failed ({rc})")
+        return out
+
+
 _default = None
 
 
@@ -231,3 +251,7 @@ def rmsnorm_f64(x, w, eps, half_x=False):
 
 def swiglu_f64(g, u):
     return _load().swiglu_f64(g, u)
+
+
+def attn_decode_f64(k_cache, v_cache, t, kv_len, n_kv, head_dim, q):
+    return _load().attn_decode_f64(k_cache, v_cache, t, kv_len, n_kv, head_dim, q)

@@ -22,6 +22,11 @@
  *        square plus eps, computed in float32, the product cast back to the
  *        input's type, then times the weight) and "SwiGLU Feed-Forward
  *        Network" (SiLU of the gate projection times the up projection).
+ *  [NL]  also section "Grouped-Query Attention (GQA) and KV Cache" (scores
+ *        q.k / sqrt(head_dim) over the cached positions, softmax, the
+ *        weighted sum of the values; query head h reads KV head h / n_rep
+ *        where n_rep = query heads per KV head) and [HG] §13.2 (the KV cache
+ *        itself stored as q8_0 or q4_0 blocks).
  *
  * Readings where the pages are silent (each one is listed in the design notes):
  *  R1 Q4_K 6-bit fields: one 96-bit little-endian stream, field k at bits
@@ -39,6 +44,10 @@
  *     exact), t = a*q (exact) and then one rounding in t - b.  Q6_K forms the
  *     integer k = sc*(q-32) first, then d*k (exact).  The others are d*(q-off)
  *     (exact).  The pages' "-> fp16" comments are not followed: fp32 is used.
+ *  R13 Quantized KV cache: K and V are each [kv_len][n_kv][head_dim], row
+ *     (t, g) = t*n_kv + g quantized along head_dim in blocks of the cache's
+ *     type (the page's cache tensor is [batch, positions, kv heads, head
+ *     dim]; blocks run along the contiguous dimension as in a weight row).
  *  R7 Quantizer (used only to make test inputs): symmetric absmax per block
  *     for Q4_0/Q5_0/Q8_0/Q6_K sub-blocks and min/scale for Q4_K, in fp64, with
  *     stored fp16 scales rounded UP so every weight is covered; codes are
@@ -54,7 +63,9 @@
  *   1 nibble order swapped, 2 Q4_K min added instead of subtracted,
  *   3 Q4_K scale/min fields swapped, 4 Q6_K offset 31 instead of 32,
  *   5 dot drops the last column, 6 dot reads x transposed,
- *   7 RMSNorm leaves out eps, 8 SiLU uses exp(+v). */
+ *   7 RMSNorm leaves out eps, 8 SiLU uses exp(+v),
+ *   9 attention scores without the 1/sqrt(head_dim) scale,
+ *   10 query head h reads KV head h % n_kv instead of h / n_rep. */
 #ifndef GQO_PLANT
 #define GQO_PLANT 0
 #endif
@@ -359,6 +370,53 @@ int gqo_swiglu_f64(const double *g, const double *u, int64_t n, double *out) {
         const double silu = v / (1.0 + exp((GQO_PLANT == 8) ? v : -v));
         out[i] = silu * u[i];
     }
+    return 0;
+}
+
+/* ---------------------------------------------------------------- attention over a quantized KV cache */
+
+int gqo_attn_decode_f64(int type, const uint8_t *k_cache, const uint8_t *v_cache, int64_t kv_len,
+                        int64_t n_kv, int64_t head_dim, const double *q, int64_t n_heads,
+                        double *out) {
+    int64_t qk, bb;
+    if (gqo_block_info(type, &qk, &bb)) return -1;
+    if (!k_cache || !v_cache || !q || !out) return -3;
+    if (kv_len < 1 || n_kv < 1 || n_heads < n_kv || n_heads % n_kv || head_dim < 1 ||
+        head_dim % qk)
+        return -2;
+    const int64_t n_rep = n_heads / n_kv, rb = head_dim / qk * bb;
+    double *kd = malloc(sizeof(double) * kv_len * head_dim);
+    double *vd = malloc(sizeof(double) * kv_len * head_dim);
+    double *s = malloc(sizeof(double) * kv_len);
+    if (!kd || !vd || !s) { free(kd); free(vd); free(s); return -4; }
+    const double scale = (GQO_PLANT == 9) ? 1.0 : 1.0 / sqrt((double)head_dim);
+    for (int64_t g = 0; g < n_kv; g++) {
+        /* the cached rows of KV head g, dequantized exactly */
+        for (int64_t t = 0; t < kv_len; t++) {
+            dequant_row_f64(type, k_cache + (t * n_kv + g) * rb, head_dim, kd + t * head_dim);
+            dequant_row_f64(type, v_cache + (t * n_kv + g) * rb, head_dim, vd + t * head_dim);
+        }
+        for (int64_t h = 0; h < n_heads; h++) {
+            const int64_t kvh = (GQO_PLANT == 10) ? h % n_kv : h / n_rep;
+            if (kvh != g) continue;
+            const double *qh = q + h * head_dim;
+            double m = -INFINITY;
+            for (int64_t t = 0; t < kv_len; t++) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < head_dim; c++) acc += qh[c] * kd[t * head_dim + c];
+                s[t] = acc * scale;
+                if (s[t] > m) m = s[t];
+            }
+            double l = 0.0;
+            for (int64_t t = 0; t < kv_len; t++) { s[t] = exp(s[t] - m); l += s[t]; }
+            for (int64_t c = 0; c < head_dim; c++) {
+                double acc = 0.0;
+                for (int64_t t = 0; t < kv_len; t++) acc += s[t] * vd[t * head_dim + c];
+                out[h * head_dim + c] = acc / l;
+            }
+        }
+    }
+    free(kd); free(vd); free(s);
     return 0;
 }
 

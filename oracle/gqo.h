@@ -59,6 +59,20 @@ int gqo_rmsnorm_f64(const double *x, int64_t cols, const double *w, double eps, 
  * out[i] = silu(g[i]) * u[i], silu(v) = v / (1 + exp(-v)), in fp64. */
 int gqo_swiglu_f64(const double *g, const double *u, int64_t n, double *out);
 
+/*
+ * One decode step of grouped-query attention over a block-quantized KV cache
+ * ("How LLM Inference Engines Work", "Grouped-Query Attention (GQA) and KV
+ * Cache"; Hitchhiker's Guide §13.2 for q8_0 / q4_0 caches), in fp64:
+ *   for query head h, g = h / (n_heads / n_kv):
+ *     s[t]   = (sum_c q[h][c] * K^[t][g][c]) / sqrt(head_dim),   t < kv_len
+ *     out[h] = sum_t softmax(s)[t] * V^[t][g]
+ * k_cache, v_cache: [kv_len][n_kv][head_dim] blobs, each (t, g) row of
+ * head_dim quantized along head_dim (reading R13).  q, out: [n_heads][head_dim].
+ */
+int gqo_attn_decode_f64(int type, const uint8_t *k_cache, const uint8_t *v_cache, int64_t kv_len,
+                        int64_t n_kv, int64_t head_dim, const double *q, int64_t n_heads,
+                        double *out);
+
 #ifdef __cplusplus
 }
 #endif

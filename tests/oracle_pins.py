@@ -15,7 +15,10 @@ What each pin rests on:
   * invariants: power-of-two scaling is exact, row permutation permutes y,
     n tokens in one call equal n calls;
   * the quantizer's round-trip error bound derived from its definition;
-  * RMSNorm and SiLU: closed forms, identities and invariants.
+  * RMSNorm and SiLU: closed forms, identities and invariants;
+  * decode attention over a quantized KV cache: closed forms (one position,
+    zero query, two positions), the query-to-KV head mapping, and invariance
+    under permuting the cached positions.
 """
 from __future__ import annotations
 
@@ -282,5 +285,73 @@ def pin_swiglu(o):
     assert np.allclose(o.swiglu_f64(v, u), sp * u, rtol=1e-15, atol=0)
 
 
+def _q8_rows(codes, d_bits=0x3C00):
+    """Q8_0 blob from int8 codes [rows][32k] with one fp16 scale per block
+    (the Hitchhiker's Guide §11.1 layout: fp16 d, then the codes); d = 1.0
+    by default (0x3C00)."""
+    codes = np.asarray(codes, dtype=np.int64)
+    rows, cols = codes.shape
+    out = bytearray()
+    for r in range(rows):
+        for b in range(cols // 32):
+            out += int(d_bits).to_bytes(2, "little")
+            out += bytes((int(v) & 0xFF) for v in codes[r, 32 * b:32 * b + 32])
+    return np.frombuffer(bytes(out), dtype=np.uint8)
+
+
+def pin_attention(o):
+    """Decode attention over a quantized KV cache ("How LLM Inference Engines
+    Work", "Grouped-Query Attention (GQA) and KV Cache") against closed
+    forms: one cached position gives its value row exactly (softmax of one
+    score is 1); a zero query scores every position 0, so the output is the
+    mean of the value rows; two positions whose scores differ by D weigh
+    their values 1 : exp(D), with D = q.k / sqrt(head_dim); when each KV
+    head's values are the constant g + 1, query head h returns
+    h // (n_heads / n_kv) + 1 (the head mapping of the page's expand); and
+    permuting the cached positions changes nothing."""
+    rng = np.random.default_rng(21)
+    hd, n_kv, n_heads = 64, 4, 8
+    # one position
+    k1 = _q8_rows(rng.integers(-127, 128, (n_kv, hd)))
+    v1 = _q8_rows(rng.integers(-127, 128, (n_kv, hd)))
+    q = rng.standard_normal((n_heads, hd))
+    out = o.attn_decode_f64(k1, v1, "q8_0", 1, n_kv, hd, q)
+    vd = o.dequant_f64(v1, "q8_0", n_kv, hd)
+    assert np.array_equal(out, vd[np.arange(n_heads) // 2]), "one position"
+    # zero query: the mean of the values
+    T = 37
+    kc = _q8_rows(rng.integers(-127, 128, (T * n_kv, hd)))
+    vc = _q8_rows(rng.integers(-127, 128, (T * n_kv, hd)))
+    out = o.attn_decode_f64(kc, vc, "q8_0", T, n_kv, hd, np.zeros((n_heads, hd)))
+    vd = o.dequant_f64(vc, "q8_0", T * n_kv, hd).reshape(T, n_kv, hd)
+    ref = vd.mean(axis=0)[np.arange(n_heads) // 2]
+    assert np.allclose(out, ref, rtol=1e-13, atol=1e-13), "zero query"
+    # two positions, one head: K0 = 0, K1 = c at dim 5; q = a at dim 5
+    c, a = 90, 0.37
+    kk = np.zeros((2, 32), dtype=np.int64)
+    kk[1, 5] = c
+    vv = np.array([[-40] * 32, [100] * 32])
+    qq = np.zeros((1, 32))
+    qq[0, 5] = a
+    out = o.attn_decode_f64(_q8_rows(kk), _q8_rows(vv), "q8_0", 2, 1, 32, qq)
+    D = a * c / np.sqrt(32.0)
+    ref = (-40.0 + 100.0 * np.exp(D)) / (1.0 + np.exp(D))
+    assert np.allclose(out, ref, rtol=1e-14, atol=0), (out[0, 0], ref)
+    # head mapping: V of KV head g is the constant g + 1
+    vg = np.array([[g + 1] * hd for t in range(T) for g in range(n_kv)])
+    out = o.attn_decode_f64(kc, _q8_rows(vg), "q8_0", T, n_kv, hd, q)
+    ref = (np.arange(n_heads) // 2 + 1.0)[:, None] * np.ones((1, hd))
+    assert np.allclose(out, ref, rtol=1e-14, atol=0), "head mapping"
+    # permutation of positions
+    perm = rng.permutation(T)
+    rb = o.row_bytes("q8_0", hd)
+    kr = kc.reshape(T, n_kv * rb)[perm].reshape(-1)
+    vr = vc.reshape(T, n_kv * rb)[perm].reshape(-1)
+    a1 = o.attn_decode_f64(kc, vc, "q8_0", T, n_kv, hd, q)
+    a2 = o.attn_decode_f64(kr, vr, "q8_0", T, n_kv, hd, q)
+    assert np.allclose(a1, a2, rtol=1e-12, atol=1e-12), "position permutation"
+
+
 ALL_PINS = [pin_golden, pin_sizes, pin_fraction_dot, pin_q8_integer, pin_q4k_structured,
-            pin_pow2_and_perm, pin_f32_is_one_rounding, pin_roundtrip, pin_rmsnorm, pin_swiglu]
+            pin_pow2_and_perm, pin_f32_is_one_rounding, pin_roundtrip, pin_rmsnorm, pin_swiglu,
+            pin_attention]
