@@ -25,12 +25,18 @@ Method:
   * secondary: the Q4_K 11008x4096 dequant-GEMM at 512 fp16 tokens (GFLOP/s
     against the 2.5 PFLOP/s dense fp16 matrix peak) and a sweep of the other
     workload shapes;
+  * attn_decode: one decode step of grouped-query attention over q8_0 and
+    q4_0 K/V caches (32k positions, 8 KV heads, head_dim 128, 40 query
+    heads), cache bytes per call / time, rotating over >= 512 MB of caches;
+  * stream_read_reference (inside roofline): the library's plain
+    streaming-read kernel at the dominant launch's size and at 1 GiB;
   * cpu_baseline: the CPU oracle (fp64 dequant-then-dot, OpenMP over rows) on
     the same layer, the oracle quantizing its own blobs from the same draws.
 
 Prints one JSON line.  `--profile-launches N` instead runs N plain (ungraphed)
 launches of each layer matrix plus a device copy of known size, and
-`--profile-gemm N` N plain launches of the 512-token GEMM, for rocprofv3
+`--profile-gemm N` N plain launches of the 512-token GEMM, `--profile-attn N` N
+plain calls of the q8_0 KV-cache attention decode, for rocprofv3
 kernel traces and counters.
 """
 from __future__ import annotations
@@ -80,6 +86,8 @@ def parse():
     p.add_argument("--profile-gemm", type=int, default=0, metavar="N",
                    help="only run N plain launches of the 512-token GEMM (for rocprofv3)")
     p.add_argument("--profile-launches", type=int, default=0)
+    p.add_argument("--profile-attn", type=int, default=0, metavar="N",
+                   help="only run N plain calls of the q8_0 KV-cache attention decode")
     return p.parse_args()
 
 
@@ -348,6 +356,68 @@ def fused_layer(mats, steps, warmup):
     return time_graphs(graphs, steps, warmup)
 
 
+# Decode attention over a quantized KV cache: the 30B-class cache of the
+# Hitchhiker's Guide §13.2 (8 KV heads, head_dim 128, 32k positions) with 40
+# query heads, one layer's K and V.
+ATTN = {"kv_len": 32768, "n_kv": 8, "n_heads": 40, "head_dim": 128}
+
+
+class AttnCase:
+    def __init__(self, t, ncopies=None, seed=9500):
+        import torch
+        import gguf_quant_matmul_amd as gq
+        a = ATTN
+        self.t = t
+        rows = a["kv_len"] * a["n_kv"]
+        gen = torch.Generator(device="cuda").manual_seed(seed)
+        k = torch.randn(rows, a["head_dim"], device="cuda", generator=gen)
+        v = torch.randn(rows, a["head_dim"], device="cuda", generator=gen)
+        kb, vb = gq.quantize(k, t), gq.quantize(v, t)
+        del k, v
+        self.cache_bytes = kb.numel() + vb.numel()
+        n = ncopies or max(2, -(-2 * CACHE_BYTES // self.cache_bytes) + 1)
+        self.copies = [(kb, vb)] + [(kb.clone(), vb.clone()) for _ in range(n - 1)]
+        self.q = torch.randn(a["n_heads"], a["head_dim"], device="cuda", generator=gen)
+        self.out = torch.empty_like(self.q)
+        need = gq.attn_decode_workspace_bytes(a["kv_len"], a["n_kv"], a["n_heads"], a["head_dim"])
+        self.ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        self.tid = gq.TYPES[t]
+
+    def launch(self, i, sp):
+        import gguf_quant_matmul_amd as gq
+        a = ATTN
+        kb, vb = self.copies[i % len(self.copies)]
+        rc = gq.lib().gq_attn_decode(kb.data_ptr(), vb.data_ptr(), self.tid, a["kv_len"], a["n_kv"],
+                                     a["head_dim"], self.q.data_ptr(), a["n_heads"],
+                                     self.out.data_ptr(), self.ws.data_ptr(), self.ws.numel(), sp)
+        if rc:
+            raise RuntimeError(f"gq_attn_decode: {gq.strerror(rc)}")
+
+
+def attn_bench(steps):
+    """Per-call time of the attention decode (both of its kernels), graph-
+    timed over rotating caches totalling >= 2x the Infinity Cache."""
+    out = []
+    for t in ("q8_0", "q4_0"):
+        c = AttnCase(t)
+        per = 8
+        graphs = []
+        for gi in range(-(-len(c.copies) // per)):
+            def fn(sp, gi=gi):
+                for j in range(per):
+                    c.launch(gi * per + j, sp)
+            graphs.append(capture(fn))
+        ms = time_graphs(graphs, max(32, steps // 2), warmup=2) / per
+        gbs = c.cache_bytes / (ms * 1e-3) / 1e9
+        out.append({"case": f"decode attention, {t} K and V caches, {ATTN['kv_len']} positions x "
+                            f"{ATTN['n_kv']} KV heads x {ATTN['head_dim']}, {ATTN['n_heads']} query heads",
+                    "cache_bytes": c.cache_bytes, "us": round(ms * 1e3, 2), "GBps": round(gbs, 1),
+                    "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        log(f"  attention {t}: {ms*1e3:.2f} us  {gbs:.1f} GB/s")
+        del c, graphs
+    return out
+
+
 def profile_launches(mats, n):
     """Plain launches for rocprofv3, in dispatch order: each layer matrix n
     times in turn (rotating copies), then n single-dispatch elementwise
@@ -381,6 +451,15 @@ def main():
 
     gq.lib()
     torch.cuda.init()
+    if args.profile_attn:
+        c = AttnCase("q8_0")
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for i in range(args.profile_attn):
+            c.launch(i, sp)
+        torch.cuda.synchronize()
+        log(f"profile: {args.profile_attn} calls of the q8_0 attention decode")
+        return
     if args.profile_gemm:
         m = Mat("gemm q4_k 11008x4096 n=512", "q4_k", [("w", 11008)], 4096, seed=9000, ncopies=1,
                 n_tok=512, x_dtype="f16")
@@ -463,6 +542,11 @@ def main():
                                   "traffic_note": "HBM bytes fetched per launch (FETCH_SIZE, "
                                                   "calibrated); writes not included"}}
 
+    attn = None
+    if not args.no_sweep:
+        log("attention decode over quantized KV caches")
+        attn = attn_bench(args.steps)
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
@@ -480,6 +564,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "attn_decode": attn,
         "fused_layer": fused,
         "per_launch": per,
         "sweep": shapes,

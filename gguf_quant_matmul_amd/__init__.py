@@ -50,6 +50,10 @@ def lib():
         L.gq_matmul_ex.restype = ci
         L.gq_matmul_decode.argtypes = [vp, vp, ci, i64, i64, vp, ci, vp, ctypes.c_float, vp, vp]
         L.gq_matmul_decode.restype = ci
+        L.gq_attn_decode_workspace_bytes.argtypes = [i64, ci, ci, ci]
+        L.gq_attn_decode_workspace_bytes.restype = i64
+        L.gq_attn_decode.argtypes = [vp, vp, ci, i64, ci, ci, vp, ci, vp, vp, i64, vp]
+        L.gq_attn_decode.restype = ci
         L.gq_probe_stream_read.argtypes = [vp, i64, vp, vp]
         L.gq_probe_stream_read.restype = ci
         L.gq_dequant.argtypes = [vp, ci, i64, i64, vp, ci, vp]
@@ -141,6 +145,36 @@ def matmul_decode(blob, t, rows: int, cols: int, x, up=None, norm_weight=None, e
                                 float(eps), out.data_ptr(), _stream(stream))
     if rc:
         raise GQError(rc, "gq_matmul_decode")
+    return out
+
+
+def attn_decode_workspace_bytes(kv_len: int, n_kv_heads: int, n_heads: int, head_dim: int) -> int:
+    n = lib().gq_attn_decode_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim)
+    if n < 0:
+        raise GQError(int(n), "gq_attn_decode_workspace_bytes")
+    return int(n)
+
+
+def attn_decode(k_cache, v_cache, t, kv_len: int, n_kv_heads: int, head_dim: int, q,
+                out=None, workspace=None, stream=None):
+    """One decode step of GQA attention over q8_0 / q4_0 K and V caches
+    (uint8 CUDA blobs, [kv_len][n_kv_heads][head_dim] rows); q fp32
+    [n_heads, head_dim].  Returns out fp32 [n_heads, head_dim]."""
+    import torch
+    if q.dtype != torch.float32:
+        raise TypeError("q must be float32")
+    q = q.contiguous()
+    n_heads = q.shape[0]
+    need = attn_decode_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((n_heads, head_dim), dtype=torch.float32, device=q.device)
+    rc = lib().gq_attn_decode(k_cache.data_ptr(), v_cache.data_ptr(), _tid(t), kv_len,
+                              n_kv_heads, head_dim, q.data_ptr(), n_heads, out.data_ptr(),
+                              workspace.data_ptr(), workspace.numel(), _stream(stream))
+    if rc:
+        raise GQError(rc, "gq_attn_decode")
     return out
 
 

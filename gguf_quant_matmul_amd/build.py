@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libgq.so")
-SOURCES = ["gq_api.cpp", "k_quant.hip", "k_gemv.hip", "k_mmv.hip", "k_gemm.hip", "k_probe.hip"]
+SOURCES = ["gq_api.cpp", "k_quant.hip", "k_gemv.hip", "k_mmv.hip", "k_gemm.hip", "k_probe.hip",
+           "k_attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

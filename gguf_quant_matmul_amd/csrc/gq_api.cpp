@@ -140,6 +140,48 @@ int gq_matmul_decode(const void* weight_blob, const void* up_blob, int ggml_type
                                           (hipStream_t)stream));
 }
 
+static int check_attn_shape(int64_t kv_len, int n_kv_heads, int n_heads, int head_dim) {
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256) return GQ_EINVAL_SHAPE;
+  if (kv_len < 1 || n_kv_heads < 1 || n_heads < n_kv_heads || n_heads % n_kv_heads ||
+      n_heads / n_kv_heads > 16)
+    return GQ_EINVAL_SHAPE;
+  if (n_kv_heads > 65535 || kv_len >= kDim) return GQ_EOVERFLOW;
+  return GQ_OK;
+}
+
+int64_t gq_attn_decode_workspace_bytes(int64_t kv_len, int n_kv_heads, int n_heads,
+                                       int head_dim) {
+  int rc = check_attn_shape(kv_len, n_kv_heads, n_heads, head_dim);
+  if (rc) return rc;
+  return gq::attn_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim);
+}
+
+int gq_attn_decode(const void* k_cache, const void* v_cache, int kv_type, int64_t kv_len,
+                   int n_kv_heads, int head_dim, const float* q, int n_heads, float* out,
+                   void* workspace, int64_t workspace_bytes, void* stream) {
+  if (kv_type != GQ_Q8_0 && kv_type != GQ_Q4_0) return GQ_EINVAL_TYPE;
+  int rc = check_attn_shape(kv_len, n_kv_heads, n_heads, head_dim);
+  if (rc) return rc;
+  const int64_t rb = gq_row_bytes(kv_type, head_dim);
+  if (kv_len > (((int64_t)1 << 31) - 1) / ((int64_t)n_kv_heads * rb)) return GQ_EOVERFLOW;
+  const int64_t need = gq::attn_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim);
+  if (workspace_bytes < need) return GQ_EINVAL_SHAPE;
+  if (!k_cache || !v_cache || !q || !out || !workspace) return GQ_EINVAL_PTR;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out) ||
+      !aligned16(workspace))
+    return GQ_EALIGN;
+  const int64_t cbytes = kv_len * n_kv_heads * rb;
+  const int64_t qbytes = (int64_t)n_heads * head_dim * 4;
+  if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_cache, cbytes) ||
+      overlap(out, qbytes, v_cache, cbytes) || overlap(out, qbytes, workspace, need) ||
+      overlap(workspace, need, q, qbytes) || overlap(workspace, need, k_cache, cbytes) ||
+      overlap(workspace, need, v_cache, cbytes))
+    return GQ_EINVAL_PTR;
+  return hip_status(gq::launch_attn_decode(kv_type, k_cache, v_cache, kv_len, n_kv_heads,
+                                           head_dim, q, n_heads, out, (float*)workspace,
+                                           (hipStream_t)stream));
+}
+
 int gq_probe_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
   if (bytes < 0 || bytes % 16) return GQ_EINVAL_SHAPE;
   if (bytes > ((int64_t)1 << 30)) return GQ_EOVERFLOW;

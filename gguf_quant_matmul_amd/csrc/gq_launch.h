@@ -21,6 +21,19 @@ hipError_t launch_gemv_fused(int type, const void* blob, const void* up_blob, in
 // Streaming read of bytes (<= 2^30, a multiple of 16) into per-workgroup
 // XORs, GQ_PROBE_OUT_WORDS of them.
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* out, hipStream_t st);
+// Decode attention over a q8_0 / q4_0 KV cache ([kv_len][n_kv][head_dim],
+// head_dim 64, 128 or 256, n_heads / n_kv <= 16): split over chunks of
+// positions, partial statistics in workspace (attn_workspace_bytes), then
+// combined.
+struct AttnPlan {
+  int chunk;
+  int64_t n_chunks;
+};
+AttnPlan attn_plan(int64_t kv_len, int n_kv, int n_rep, int head_dim);
+int64_t attn_workspace_bytes(int64_t kv_len, int n_kv, int n_heads, int head_dim);
+hipError_t launch_attn_decode(int kv_type, const void* k_cache, const void* v_cache,
+                              int64_t kv_len, int n_kv, int head_dim, const float* q,
+                              int n_heads, float* out, float* workspace, hipStream_t st);
 // Small batches: the weight stream on the matrix cores, 16 tokens per pass.
 hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                       bool x_f16, float* y, int64_t n_tok, hipStream_t st);

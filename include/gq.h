@@ -177,6 +177,37 @@ int gq_quantize(const float *w, int ggml_type, int64_t rows, int64_t cols,
                 void *weight_blob, void *stream);
 
 /*
+ * One decode step of grouped-query attention over a KV cache stored as q8_0
+ * or q4_0 blocks ("How LLM Inference Engines Work", section "Grouped-Query
+ * Attention (GQA) and KV Cache"; the cache types of the Hitchhiker's Guide
+ * §13.2).  For query head h and its KV head g = h / (n_heads / n_kv_heads):
+ *     s[t]   = (sum_c q[h][c] * K^[t][g][c]) / sqrt(head_dim)     in fp32
+ *     out[h] = sum_t softmax(s)[t] * V^[t][g]                     in fp32
+ * over the cached positions t < kv_len, K^ and V^ the dequantized caches.
+ *   k_cache, v_cache  device, [kv_len][n_kv_heads][head_dim] as a blob of
+ *                     kv_len*n_kv_heads rows of head_dim weights quantized
+ *                     along head_dim (row (t, g) = t*n_kv_heads + g,
+ *                     gq_row_bytes(kv_type, head_dim) bytes each); read only
+ *   kv_type           GQ_Q8_0 or GQ_Q4_0 (both caches)
+ *   head_dim          64, 128 or 256; n_heads a multiple of n_kv_heads with
+ *                     at most 16 query heads per KV head; kv_len >= 1
+ *   q                 device fp32 [n_heads][head_dim]; out device fp32
+ *                     [n_heads][head_dim], overwritten
+ *   workspace         device, at least gq_attn_decode_workspace_bytes(...)
+ *                     bytes (per-chunk softmax statistics), contents ignored
+ *                     and overwritten; one per concurrent call
+ * All pointers 16-byte aligned; out and workspace overlap nothing else.  The
+ * cache must stay below 2^31 bytes (GQ_EOVERFLOW).  The result does not
+ * depend on the run: positions are split into fixed chunks and combined in
+ * order.
+ */
+int64_t gq_attn_decode_workspace_bytes(int64_t kv_len, int n_kv_heads, int n_heads,
+                                       int head_dim);
+int gq_attn_decode(const void *k_cache, const void *v_cache, int kv_type, int64_t kv_len,
+                   int n_kv_heads, int head_dim, const float *q, int n_heads, float *out,
+                   void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * Measurement: a plain streaming read of `bytes` bytes of device memory at
  * buf with 128-bit loads, every byte read once, nothing else done.  Its
  * bandwidth is the practical ceiling the GEMV kernels' effective bandwidth

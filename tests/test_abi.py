@@ -113,3 +113,33 @@ def test_probe_validation():
     assert L.gq_probe_stream_read(A, 64, None, None) == -3
     assert L.gq_probe_stream_read(A + 8, 64, B, None) == -4
     assert L.gq_probe_stream_read(A, 64, A + 32, None) == -3       # out overlaps buf
+
+
+def test_attn_workspace_and_validation():
+    L = gq.lib()
+    # 32k positions, 8 KV heads, 40 query heads, head_dim 128: 128 chunks of 256
+    assert L.gq_attn_decode_workspace_bytes(32768, 8, 40, 128) == 128 * 40 * 130 * 4
+    assert L.gq_attn_decode_workspace_bytes(1, 1, 1, 64) == 1 * 1 * 66 * 4
+    assert L.gq_attn_decode_workspace_bytes(10, 8, 44, 128) == -2     # heads not a multiple
+    assert L.gq_attn_decode_workspace_bytes(10, 2, 34, 128) == -2     # 17 query heads per KV head
+    assert L.gq_attn_decode_workspace_bytes(10, 2, 4, 96) == -2       # head_dim
+    assert L.gq_attn_decode_workspace_bytes(0, 2, 4, 128) == -2       # no positions
+    K, V, Q, O, WS = 0x100000, 0x200000, 0x300000, 0x310000, 0x400000
+    ok = (K, V, gq.Q8_0, 100, 2, 128, Q, 8, O, WS, 1 << 20, None)
+
+    def call(**kw):
+        names = ["k", "v", "t", "n", "nkv", "hd", "q", "nh", "o", "ws", "wsb", "s"]
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return L.gq_attn_decode(*[a[n] for n in names])
+
+    assert call(t=gq.Q4_K) == -1
+    assert call(t=gq.F16) == -1
+    assert call(hd=96) == -2
+    assert call(nh=7) == -2 and call(nh=34, nkv=2) == -2
+    assert call(wsb=100) == -2                                        # workspace too small
+    assert call(k=None) == -3 and call(ws=None) == -3
+    assert call(v=V + 4) == -4 and call(o=O + 8) == -4
+    assert call(o=Q + 64) == -3                                       # out overlaps q
+    assert call(ws=K + 256) == -3                                     # workspace overlaps the K cache
+    assert call(n=1 << 28, nkv=8) == -5                               # cache beyond 2^31 bytes
