@@ -28,6 +28,18 @@ constexpr int ATT_LDS = 65536;            // LDS budget of the part kernel
 // Largest chunk (positions) for NB blocks per row.
 constexpr int ATT_CHUNK_CAP(int nb) { return nb > 4 ? 128 : 256; }
 
+// Bytes of lo (0..3) and hi (4..7) as the fp16 values 1024 + byte (fp16 has
+// unit spacing on [1024, 2048), so the bytes go straight into the low
+// mantissa bits under the exponent byte 0x64).
+__device__ __forceinline__ f16x8 bytes_1024(uint32_t lo, uint32_t hi) {
+  const uint32_t e = 0x64646464u;
+  const uint32_t w0 = __builtin_amdgcn_perm(e, lo, 0x04010400u);
+  const uint32_t w1 = __builtin_amdgcn_perm(e, lo, 0x04030402u);
+  const uint32_t w2 = __builtin_amdgcn_perm(e, hi, 0x04010400u);
+  const uint32_t w3 = __builtin_amdgcn_perm(e, hi, 0x04030402u);
+  return __builtin_bit_cast(f16x8, u32x4{w0, w1, w2, w3});
+}
+
 template <int KT> struct KvBlock;
 
 template <> struct KvBlock<GQ_Q8_0> {          // fp16 d, 32 int8 codes
@@ -39,18 +51,13 @@ template <> struct KvBlock<GQ_Q8_0> {          // fp16 d, 32 int8 codes
   __device__ static Raw load(__amdgpu_buffer_rsrc_t r, int o) {
     return Raw{bld16(r, o, 2), bld16(r, o, 18), bld2(r, o, 0)};
   }
-  // the 32 codes as exact fp32; returns the block scale
-  __device__ static float decode(const Raw& raw, float (&c)[32]) {
-    const u32x4 a = raw.a, b = raw.b;
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int i = 0; i < 8; i++) {
-      c[4 * i] = sb0(w[i]);
-      c[4 * i + 1] = sb1(w[i]);
-      c[4 * i + 2] = sb2(w[i]);
-      c[4 * i + 3] = sb3(w[i]);
-    }
-    return h2f(raw.d);
+  // A lane's matrix-core share of a staged block: codes 8g .. 8g + 7 (at
+  // byte frag_off(g) of the block's codes) as exact fp16,
+  // (1024 + (q + 128)) - 1152.
+  __device__ static int frag_off(int g) { return 8 * g; }
+  __device__ static f16x8 frag_codes(u32x2 c, int) {
+    const f16x8 v = bytes_1024(c.x ^ 0x80808080u, c.y ^ 0x80808080u);
+    return v - (_Float16)1152.f;
   }
   static constexpr int CODE_BYTES = 32;
   __device__ static void store_codes(const Raw& raw, uint8_t* p) {     // 16-byte aligned
@@ -74,22 +81,13 @@ template <> struct KvBlock<GQ_Q4_0> {          // fp16 d, 16 bytes: low nibbles 
     uint32_t d;
   };
   __device__ static Raw load(__amdgpu_buffer_rsrc_t r, int o) { return Raw{bld16(r, o, 2), bld2(r, o, 0)}; }
-  __device__ static float decode(const Raw& raw, float (&c)[32]) {
-    const u32x4 a = raw.a;
-    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const uint32_t lo = w[i] & 0x0F0F0F0Fu, hi = (w[i] >> 4) & 0x0F0F0F0Fu;
-      c[4 * i] = ub0(lo) - 8.f;
-      c[4 * i + 1] = ub1(lo) - 8.f;
-      c[4 * i + 2] = ub2(lo) - 8.f;
-      c[4 * i + 3] = ub3(lo) - 8.f;
-      c[16 + 4 * i] = ub0(hi) - 8.f;
-      c[16 + 4 * i + 1] = ub1(hi) - 8.f;
-      c[16 + 4 * i + 2] = ub2(hi) - 8.f;
-      c[16 + 4 * i + 3] = ub3(hi) - 8.f;
-    }
-    return h2f(raw.d);
+  // elements 8g .. 8g + 7: low nibbles of bytes 8g.. for g < 2, high
+  // nibbles of bytes 8(g - 2).. for g >= 2
+  __device__ static int frag_off(int g) { return 8 * (g & 1); }
+  __device__ static f16x8 frag_codes(u32x2 c, int g) {
+    const int sh = (g & 2) ? 4 : 0;
+    const f16x8 v = bytes_1024((c.x >> sh) & 0x0F0F0F0Fu, (c.y >> sh) & 0x0F0F0F0Fu);
+    return v - (_Float16)1032.f;
   }
   static constexpr int CODE_BYTES = 16;
   __device__ static void store_codes(const Raw& raw, uint8_t* p) {
@@ -129,7 +127,7 @@ __host__ __device__ inline AttnLds attn_lds(int n_rep, int nrp, int chunk, int n
 
 // Query heads per KV head rounded up to the accumulator count compiled in.
 __host__ __device__ inline int attn_nrp(int n_rep) {
-  return n_rep <= 1 ? 1 : n_rep <= 2 ? 2 : n_rep <= 4 ? 4 : n_rep <= 8 ? 8 : 16;
+  return n_rep <= 2 ? n_rep : n_rep <= 4 ? 4 : n_rep <= 5 ? 5 : n_rep <= 8 ? 8 : 16;
 }
 
 template <int KT, int NB, int NRP>
@@ -158,11 +156,9 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
 
   // Every load of the chunk goes out first, so the workgroup waits one
   // memory latency: the V blocks (one block per thread and round; blocks
-  // past the chunk's end read as zero) and, for the scores, NB lanes per
-  // position with lane b on block b of the K row.
+  // past the chunk's end read as zero) and the K fragments of the scores.
   constexpr int CAP = ATT_CHUNK_CAP(NB);
-  constexpr int PPW = 64 / NB;                       // positions per wave and step
-  constexpr int STEPS = CAP / (4 * PPW);
+  constexpr int TILES = CAP / 64;                    // 16-position tiles per wave
   constexpr int VIT = CAP * NB / 256;
   typename KB::Raw vr[VIT];
 #pragma unroll
@@ -171,13 +167,22 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
     const int o = (lp < cnt) ? (int)(((int64_t)(t0 + lp) * n_kv + g) * RB + b * BB) : kOobOff;
     vr[it] = KB::load(rv, o);
   }
-  const int b = lane % NB, sub = lane / NB;
-  typename KB::Raw kr[STEPS];
+  // K for the scores on the matrix cores: tiles of 16 positions, wave w
+  // taking tiles w, w + 4, ...; lane l holds position l % 16 of the tile and
+  // codes 8(l / 16) .. 8(l / 16) + 7 of every block, with the block scales
+  const int mn = lane & 15, kg = lane >> 4;
+  u32x2 kc8[TILES][NB];
+  uint32_t kd[TILES][NB];
 #pragma unroll
-  for (int s = 0; s < STEPS; s++) {
-    const int lp = wave * PPW + s * 4 * PPW + sub;
+  for (int s = 0; s < TILES; s++) {
+    const int lp = 16 * (wave + 4 * s) + mn;
     const int row = t0 + min(lp, cnt - 1);       // lanes past the chunk repeat its last row
-    kr[s] = KB::load(rk, (int)(((int64_t)row * n_kv + g) * RB + b * BB));
+    const int o = (int)(((int64_t)row * n_kv + g) * RB);
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) {
+      kc8[s][bb] = bld8(rk, o + bb * BB, 2 + KB::frag_off(kg));
+      kd[s][bb] = bld2(rk, o + bb * BB, 0);
+    }
   }
   for (int i = tid; i < n_rep * HD; i += 256) qs[i] = q[g * n_rep * HD + i];
 #pragma unroll
@@ -190,30 +195,45 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
   }
   __syncthreads();
 
-  // scores s = (q . K^) / sqrt(head_dim): exact integer codes times q, then
-  // the block scale, then the NB blocks on the cross-lane network
+  // scores s = (q . K^) / sqrt(head_dim) as 16 heads x 16 positions tiles of
+  // v_mfma_f32_16x16x32_f16, one 32-element block per step: A = the query
+  // rows' block as two fp16 parts (hi + lo, ~22 bits of each fp32 q), B =
+  // the block's codes (exact in fp16); each step's product is scaled by the
+  // block scale of its position (exact in fp32 up to one rounding) and
+  // summed in fp32.  Lane l of a result holds heads 4(l/16) .. +3 of
+  // position l % 16.
+  f16x8 qh[NB], ql[NB];
 #pragma unroll
-  for (int s = 0; s < STEPS; s++) {
-    const int base = wave * PPW + s * 4 * PPW;
-    if (base >= chunk) break;
-    const int lp = base + sub;
-    float cv[32];
-    const float d = KB::decode(kr[s], cv);
-    for (int r = 0; r < n_rep; r++) {
-      const float* qr = qs + r * HD + 32 * b;
-      float acc = 0.f;
+  for (int bb = 0; bb < NB; bb++) {
+    const float* const qr = qs + mn * HD + 32 * bb + 8 * kg;
 #pragma unroll
-      for (int k = 0; k < 32; k += 4) {
-        const f32x4 qv = *reinterpret_cast<const f32x4*>(qr + k);
-        acc = fmaf(cv[k], qv.x, acc);
-        acc = fmaf(cv[k + 1], qv.y, acc);
-        acc = fmaf(cv[k + 2], qv.z, acc);
-        acc = fmaf(cv[k + 3], qv.w, acc);
-      }
-      float sv = acc * d;
+    for (int i = 0; i < 8; i++) {
+      const float v = (mn < n_rep) ? qr[i] : 0.f;
+      const _Float16 hi = (_Float16)v;
+      qh[bb][i] = hi;
+      ql[bb][i] = (_Float16)(v - (float)hi);
+    }
+  }
 #pragma unroll
-      for (int m = 1; m < NB; m <<= 1) sv += __shfl_xor(sv, m, 64);
-      if (b == 0 && lp < chunk) sc[r * chunk + lp] = (lp < cnt) ? sv * scale : -INFINITY;
+  for (int s = 0; s < TILES; s++) {
+    const int tile = wave + 4 * s;
+    if (16 * tile >= chunk) break;
+    f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int bb = 0; bb < NB; bb++) {
+      const f16x8 B = KB::frag_codes(kc8[s][bb], kg);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[bb], B, z, 0, 0, 0);
+      D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[bb], B, D, 0, 0, 0);
+      const float ds = h2f(kd[s][bb]);
+#pragma unroll
+      for (int v = 0; v < 4; v++) sv[v] = fmaf(D[v], ds, sv[v]);
+    }
+    const int lp = 16 * tile + mn;
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int r = 4 * kg + v;
+      if (r < n_rep && lp < chunk) sc[r * chunk + lp] = (lp < cnt) ? sv[v] * scale : -INFINITY;
     }
   }
   __syncthreads();
@@ -303,11 +323,12 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
   }
 }
 
-// out[h][d] from the per-chunk statistics, in a fixed order: the largest
-// chunk max M (a tree over thread-strided maxima), then, for every output
-// column, the sums over chunks of e^(m_c - M) acc_c and e^(m_c - M) l_c,
-// each thread taking every S-th chunk (S = 256 / hd) with its loads
-// independent of one another, the S partial sums added in slice order.
+// out[h][d] from the per-chunk statistics, in a fixed order.  Workgroup
+// (h, column slice of 32): the largest chunk max M (a tree over
+// thread-strided maxima), then, for its 32 columns, the sums over chunks of
+// e^(m_c - M) acc_c and e^(m_c - M) l_c, each of the 8 threads of a column
+// taking every 8th chunk (their loads independent of one another), the 8
+// partial sums added in slice order.
 __global__ void __launch_bounds__(256) k_attn_combine(const float* __restrict__ part,
                                                       int n_chunks, int n_heads, int hd,
                                                       float* __restrict__ out) {
@@ -325,10 +346,10 @@ __global__ void __launch_bounds__(256) k_attn_combine(const float* __restrict__ 
   }
   mx = red[0];
   __syncthreads();
-  const int S = 256 / hd, d = tid % hd, sl = tid / hd;
+  const int d = 32 * blockIdx.y + (tid & 31), sl = tid >> 5;
   float num = 0.f, den = 0.f;
-#pragma unroll 8
-  for (int c = sl; c < n_chunks; c += S) {
+#pragma unroll 4
+  for (int c = sl; c < n_chunks; c += 8) {
     const float* const p = p0 + c * stride;
     const float w = expf(p[hd] - mx);
     num = fmaf(w, p[d], num);
@@ -338,9 +359,9 @@ __global__ void __launch_bounds__(256) k_attn_combine(const float* __restrict__ 
   rden[tid] = den;
   __syncthreads();
   if (sl == 0) {
-    for (int k = 1; k < S; k++) {
-      num += red[k * hd + d];
-      den += rden[k * hd + d];
+    for (int k = 1; k < 8; k++) {
+      num += red[32 * k + (tid & 31)];
+      den += rden[32 * k + (tid & 31)];
     }
     out[(int64_t)h * hd + d] = num / den;
   }
@@ -387,7 +408,7 @@ static hipError_t attn_t(const void* k_cache, const void* v_cache, int64_t kv_le
                      p.chunk, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)n_heads), dim3(256), 0, st, part,
+  hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)n_heads, HD / 32), dim3(256), 0, st, part,
                      (int)p.n_chunks, n_heads, HD, out);
   return hipGetLastError();
 }
@@ -399,6 +420,7 @@ static hipError_t attn_rep(const void* k_cache, const void* v_cache, int64_t kv_
     case 1: return attn_t<KT, NB, 1>(k_cache, v_cache, kv_len, n_kv, q, n_heads, out, part, st);
     case 2: return attn_t<KT, NB, 2>(k_cache, v_cache, kv_len, n_kv, q, n_heads, out, part, st);
     case 4: return attn_t<KT, NB, 4>(k_cache, v_cache, kv_len, n_kv, q, n_heads, out, part, st);
+    case 5: return attn_t<KT, NB, 5>(k_cache, v_cache, kv_len, n_kv, q, n_heads, out, part, st);
     case 8: return attn_t<KT, NB, 8>(k_cache, v_cache, kv_len, n_kv, q, n_heads, out, part, st);
     default: return attn_t<KT, NB, 16>(k_cache, v_cache, kv_len, n_kv, q, n_heads, out, part, st);
   }
