@@ -270,15 +270,19 @@ def cpu_baseline(layer_mats):
         blob = np.concatenate([oracle.quantize(w, m.t) for w in m.w])   # the oracle's own blobs
         work.append((m, blob, m.x_host))
     total = sum(b.size for _, b, _ in work)
-    res = {}
-    for th in (1, threads):
+    # repetitions of the whole layer until ~3 s (one thread) and ~8 s (all
+    # threads) have passed, at least 3 each: about 10 s of wall time
+    res, reps = {}, {}
+    for th, budget in ((1, 3.0), (threads, 8.0)):
         ts = []
-        for _ in range(3 if th > 1 else 1):
+        t_start = time.perf_counter()
+        while len(ts) < 3 or time.perf_counter() - t_start < budget:
             t0 = time.perf_counter()
             for m, b, x in work:
                 oracle.matmul_f64(b, m.t, m.rows, m.cols, x, threads=th)
             ts.append(time.perf_counter() - t0)
         res[th] = float(np.median(ts))
+        reps[th] = len(ts)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as fh:
@@ -292,8 +296,9 @@ def cpu_baseline(layer_mats):
         "value": round(total / res[threads] / 1e9, 3), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": f"the whole layer (4 matrices, {total} blob bytes) per repetition, fp64 "
-                  f"dequant-then-dot, median of 3 on {threads} threads; 1 thread: "
-                  f"{round(total / res[1] / 1e9, 3)} GB/s ({res[1]:.2f} s); CPU: {cpu}",
+                  f"dequant-then-dot, median of {reps[threads]} repetitions on {threads} threads; "
+                  f"1 thread: {round(total / res[1] / 1e9, 3)} GB/s (median of {reps[1]}, "
+                  f"{res[1]:.2f} s each); CPU: {cpu}",
     }
 
 
