@@ -48,6 +48,8 @@ def lib():
         L.gq_matmul.restype = ci
         L.gq_matmul_ex.argtypes = [vp, ci, i64, i64, vp, ci, vp, i64, vp]
         L.gq_matmul_ex.restype = ci
+        L.gq_matmul_path.argtypes = [vp, ci, i64, i64, vp, ci, vp, i64, ci, vp]
+        L.gq_matmul_path.restype = ci
         L.gq_matmul_decode.argtypes = [vp, vp, ci, i64, i64, vp, ci, vp, ctypes.c_float, vp, vp]
         L.gq_matmul_decode.restype = ci
         L.gq_attn_decode_workspace_bytes.argtypes = [i64, ci, ci, ci]
@@ -104,8 +106,12 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def matmul(blob, t, rows: int, cols: int, x, out=None, stream=None):
-    """y[n, rows] = W^ x for x [n, cols] (fp32 or fp16, CUDA).  fp32 result."""
+PATH_AUTO, PATH_GEMV, PATH_WEIGHT_STREAM, PATH_TILED = range(4)
+
+
+def matmul(blob, t, rows: int, cols: int, x, out=None, stream=None, path: int = PATH_AUTO):
+    """y[n, rows] = W^ x for x [n, cols] (fp32 or fp16, CUDA).  fp32 result.
+    path: the kernel family (gq_matmul_path); PATH_AUTO chooses."""
     import torch
     if x.dim() == 1:
         x = x.unsqueeze(0)
@@ -116,10 +122,10 @@ def matmul(blob, t, rows: int, cols: int, x, out=None, stream=None):
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     xt = F16 if x.dtype == torch.float16 else F32
-    rc = lib().gq_matmul_ex(blob.data_ptr(), _tid(t), rows, cols, x.data_ptr(), xt,
-                            out.data_ptr(), n, _stream(stream))
+    rc = lib().gq_matmul_path(blob.data_ptr(), _tid(t), rows, cols, x.data_ptr(), xt,
+                              out.data_ptr(), n, int(path), _stream(stream))
     if rc:
-        raise GQError(rc, "gq_matmul_ex")
+        raise GQError(rc, "gq_matmul_path")
     return out
 
 

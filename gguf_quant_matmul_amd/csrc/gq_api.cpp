@@ -39,6 +39,26 @@ int check_matrix(int type, int64_t rows, int64_t cols, int64_t* rb) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_EHIP; }
 
+// Past 64 tokens: the matrix-core GEMM walks every tile's whole K range, so
+// its time is ~ K steps x step time whenever its tiles (256 rows x 128
+// tokens) leave CUs idle, while the weight-stream kernel's time grows with
+// the number of 16-token passes.  Measured on MI355X: a K step takes ~1.0 us
+// (1.8 us for Q6_K) and a 16-token pass of the weight-stream kernel streams
+// rows*cols weights at ~150 (Q6_K ~118) TFLOP/s.  The batch goes to the
+// weight-stream kernel in ceil(n/64) near-equal chunks (each of 33 to 64
+// tokens) when that estimate is lower.
+bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_tok) {
+  const double step_us = (type == GQ_Q6_K) ? 1.8 : 1.0;
+  const double rate = (type == GQ_Q6_K) ? 118e12 : 150e12;
+  const int64_t tiles = (rows + 255) / 256 * ((n_tok + 127) / 128);
+  const double gemm_us = (double)((tiles + 255) / 256) * (double)((cols + 63) / 64) * step_us;
+  const double pass_us = (double)rows * (double)cols * 32.0 / rate * 1e6;
+  const int64_t k = (n_tok + 63) / 64, base = n_tok / k, extra = n_tok % k;
+  const int64_t passes = extra * ((base + 16) / 16) + (k - extra) * ((base + 15) / 16);
+  const double mmv_us = (double)passes * pass_us;
+  return mmv_us < gemm_us;
+}
+
 }  // namespace
 
 extern "C" {
@@ -82,13 +102,17 @@ const char* gq_strerror(int code) {
   return "unknown error code";
 }
 
-int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols,
-                 const void* x, int x_type, float* y, int64_t n_tok, void* stream) {
+int gq_matmul_path(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols,
+                   const void* x, int x_type, float* y, int64_t n_tok, int path, void* stream) {
   int64_t rb = 0;
   int rc = check_matrix(ggml_type, rows, cols, &rb);
   if (rc) return rc;
   if (x_type != GQ_F32 && x_type != GQ_F16) return GQ_EINVAL_TYPE;
   if (n_tok < 0) return GQ_EINVAL_SHAPE;
+  if (path < GQ_PATH_AUTO || path > GQ_PATH_TILED) return GQ_EINVAL_SHAPE;
+  if (path == GQ_PATH_GEMV && n_tok != 1) return GQ_EINVAL_SHAPE;
+  if ((path == GQ_PATH_WEIGHT_STREAM || path == GQ_PATH_TILED) && n_tok < 2 && n_tok != 0)
+    return GQ_EINVAL_SHAPE;
   if (n_tok >= kDim) return GQ_EOVERFLOW;
   if (n_tok == 0) return GQ_OK;
   if (n_tok == 1 && cols > kMaxColsGemv) return GQ_EOVERFLOW;
@@ -105,9 +129,29 @@ int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t c
   hipStream_t st = (hipStream_t)stream;
   const bool xf16 = (x_type == GQ_F16);
   if (n_tok == 1) return hip_status(gq::launch_gemv(ggml_type, weight_blob, rows, cols, x, xf16, y, st));
-  if (n_tok <= kSmallBatch)
-    return hip_status(gq::launch_mmv(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
-  return hip_status(gq::launch_gemm(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
+  if (path == GQ_PATH_AUTO)
+    path = (n_tok <= kSmallBatch || small_batch_chunks_faster(ggml_type, rows, cols, n_tok))
+               ? GQ_PATH_WEIGHT_STREAM
+               : GQ_PATH_TILED;
+  if (path == GQ_PATH_TILED)
+    return hip_status(gq::launch_gemm(ggml_type, weight_blob, rows, cols, x, xf16, y, n_tok, st));
+  // weight stream: ceil(n / 64) near-equal chunks of at most 64 tokens
+  const int64_t xrow = cols * (xf16 ? 2 : 4);
+  const int64_t k = (n_tok + kSmallBatch - 1) / kSmallBatch, base = n_tok / k;
+  for (int64_t c = 0, t0 = 0; c < k; c++) {
+    const int64_t nc = base + (c < n_tok % k ? 1 : 0);
+    const hipError_t e = gq::launch_mmv(ggml_type, weight_blob, rows, cols,
+                                        (const uint8_t*)x + t0 * xrow, xf16, y + t0 * rows, nc, st);
+    if (e != hipSuccess) return GQ_EHIP;
+    t0 += nc;
+  }
+  return GQ_OK;
+}
+
+int gq_matmul_ex(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols,
+                 const void* x, int x_type, float* y, int64_t n_tok, void* stream) {
+  return gq_matmul_path(weight_blob, ggml_type, rows, cols, x, x_type, y, n_tok, GQ_PATH_AUTO,
+                        stream);
 }
 
 int gq_matmul(const void* weight_blob, int ggml_type, int64_t rows, int64_t cols, const void* x,

@@ -130,6 +130,28 @@ int gq_matmul_ex(const void *weight_blob, int ggml_type, int64_t rows, int64_t c
                  const void *x, int x_type, float *y, int64_t n_tok, void *stream);
 
 /*
+ * gq_matmul_ex with the kernel family chosen by the caller (for tests,
+ * tuning and callers that know their shapes):
+ *   GQ_PATH_AUTO           what gq_matmul_ex does: n_tok = 1 -> the batch-1
+ *                          GEMV; up to 64 tokens -> the weight-stream
+ *                          kernel; more -> the tiled matrix-core GEMM, or
+ *                          the weight-stream kernel over ceil(n_tok / 64)
+ *                          near-equal chunks when a cost estimate (the
+ *                          GEMM's tiles walk the whole K range each, so
+ *                          with few tiles it leaves CUs idle) says that is
+ *                          faster;
+ *   GQ_PATH_GEMV           n_tok must be 1;
+ *   GQ_PATH_WEIGHT_STREAM  n_tok >= 2, in chunks of at most 64 tokens;
+ *   GQ_PATH_TILED          n_tok >= 2, the tiled GEMM.
+ * Results differ between paths only within the stated tolerance; each path
+ * is deterministic.  A path that does not fit n_tok, or an unknown path:
+ * GQ_EINVAL_SHAPE.  Other errors as for gq_matmul_ex.
+ */
+enum { GQ_PATH_AUTO = 0, GQ_PATH_GEMV = 1, GQ_PATH_WEIGHT_STREAM = 2, GQ_PATH_TILED = 3 };
+int gq_matmul_path(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
+                   const void *x, int x_type, float *y, int64_t n_tok, int path, void *stream);
+
+/*
  * One decode token through a transformer sublayer's projection, with the
  * steps on either side fused into the same launch:
  *   xin = norm_weight ? RMSNorm(x) : x, where RMSNorm follows "How LLM

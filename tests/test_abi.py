@@ -143,3 +143,15 @@ def test_attn_workspace_and_validation():
     assert call(o=Q + 64) == -3                                       # out overlaps q
     assert call(ws=K + 256) == -3                                     # workspace overlaps the K cache
     assert call(n=1 << 28, nkv=8) == -5                               # cache beyond 2^31 bytes
+
+
+def test_matmul_path_validation():
+    L = gq.lib()
+    args = (A, gq.Q4_K, 16, 256, B, gq.F32, 0x30000)
+    assert L.gq_matmul_path(*args, 2, gq.PATH_GEMV, None) == -2          # GEMV needs one token
+    assert L.gq_matmul_path(*args, 1, gq.PATH_TILED, None) == -2         # batched paths need two
+    assert L.gq_matmul_path(*args, 1, gq.PATH_WEIGHT_STREAM, None) == -2
+    assert L.gq_matmul_path(*args, 2, 7, None) == -2                     # unknown path
+    assert L.gq_matmul_path(*args, 2, -1, None) == -2
+    assert L.gq_matmul_path(A, gq.Q4_K, 16, 100, B, gq.F32, 0x30000, 2, gq.PATH_TILED, None) == -2
+    assert L.gq_matmul_path(*args, 0, gq.PATH_TILED, None) == 0          # no tokens: no-op

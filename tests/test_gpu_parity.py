@@ -146,6 +146,10 @@ def test_mfma_parity(t, xdt):
         x = synth.activations(n, cols, seed=40 + n, dtype=xdt)
         y = gq.matmul(bd, t, rows, cols, to_dev(x)).cpu().numpy()
         check_matmul(y, blob, t, rows, cols, x, label=f"{t} n={n} {xdt}")
+        if n > 64:                               # both kernel families past 64 tokens
+            for path in (gq.PATH_WEIGHT_STREAM, gq.PATH_TILED):
+                y = gq.matmul(bd, t, rows, cols, to_dev(x), path=path).cpu().numpy()
+                check_matmul(y, blob, t, rows, cols, x, label=f"{t} n={n} {xdt} path {path}")
 
 
 @pytest.mark.parametrize("t", gq.QUANT_TYPES)
@@ -195,7 +199,7 @@ def test_gemm_few_tiles(t, rows, cols, n, xdt):
     say(f"gemm few tiles {t} {rows}x{cols} n={n} x={xdt}")
     x = synth.activations(n, cols, seed=92, dtype=xdt)
     xd = to_dev(x)
-    ys = [gq.matmul(bd, t, rows, cols, xd).cpu().numpy() for _ in range(3)]
+    ys = [gq.matmul(bd, t, rows, cols, xd, path=gq.PATH_TILED).cpu().numpy() for _ in range(3)]
     for y in ys[1:]:
         assert np.array_equal(y.view(np.uint32), ys[0].view(np.uint32))
     check_matmul(ys[0], blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
@@ -214,12 +218,34 @@ def test_gemm_partial_wave_full_size(t, rows, cols, n):
     say(f"gemm partial wave {t} {rows}x{cols} n={n}")
     x = synth.activations(n, cols, seed=94, dtype="f16")
     xd = to_dev(x)
-    y0 = gq.matmul(bd, t, rows, cols, xd).cpu().numpy()
-    y1 = gq.matmul(bd, t, rows, cols, xd).cpu().numpy()
+    y0 = gq.matmul(bd, t, rows, cols, xd, path=gq.PATH_TILED).cpu().numpy()
+    y1 = gq.matmul(bd, t, rows, cols, xd, path=gq.PATH_TILED).cpu().numpy()
     assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
     rng = np.random.default_rng(95)
     idx = np.unique(np.concatenate([rng.choice(rows, 96, replace=False), np.r_[0:16, rows - 16:rows]]))
     check_matmul(y0, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n}")
+
+
+@pytest.mark.parametrize("t,rows,cols,n,xdt", [
+    ("q6_k", 4096, 14336, 128, "f16"),   # few GEMM tiles over a long K: two 64-token chunks
+    ("q4_k", 4096, 4096, 65, "f16"),     # chunks of 33 and 32
+    ("q4_k", 1024, 4096, 130, "f32"),    # three chunks (44, 43, 43), fp32 x
+])
+def test_batch_chunks_past_64_tokens(t, rows, cols, n, xdt):
+    """Past 64 tokens on shapes with few GEMM tiles the automatic choice runs
+    the weight-stream kernel in chunks: bit-identical to asking for that path,
+    and against the oracle on sampled rows (all tokens)."""
+    _, blob = quantized(t, rows, cols, seed=301)
+    bd = to_dev(blob)
+    say(f"batch chunks {t} {rows}x{cols} n={n} x={xdt}")
+    x = synth.activations(n, cols, seed=302, dtype=xdt)
+    xd = to_dev(x)
+    ya = gq.matmul(bd, t, rows, cols, xd).cpu().numpy()
+    yw = gq.matmul(bd, t, rows, cols, xd, path=gq.PATH_WEIGHT_STREAM).cpu().numpy()
+    assert np.array_equal(ya.view(np.uint32), yw.view(np.uint32))
+    rng = np.random.default_rng(303)
+    idx = np.unique(np.concatenate([rng.choice(rows, 64, replace=False), np.r_[0:8, rows - 8:rows]]))
+    check_matmul(ya, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n} {xdt}")
 
 
 # ---------------------------------------------------------------- decode-layer fusions
