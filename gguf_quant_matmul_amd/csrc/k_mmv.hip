@@ -1,6 +1,6 @@
 // k_mmv.hip — small-batch matmul over GGUF blocks (2 <= n_tok, a few token
-// passes of 16) on the gfx950 matrix cores.  Each weight is decoded once per
-// 16-token pass and reused for every token of the pass ("Local LLM
+// passes of 8, 16 or 32) on the gfx950 matrix cores.  Each weight is decoded
+// once per pass and reused for every token of the pass ("Local LLM
 // inference", "The mmap backend"); with so few tokens the work is still
 // bound by the weight stream ("12 — llama.cpp / GGUF", "The bandwidth cap"),
 // so the kernel is built around keeping enough weight bytes in flight:
@@ -18,7 +18,8 @@
 //     directly in A layout would touch 64 lines per instruction, and the
 //     per-CU load pipeline, not HBM, would then set the speed;
 //   * the contraction is v_mfma_f32_16x16x32_f16 with A = 16 tokens x 32 k of
-//     x and B = 32 k x 16 rows of decoded weights.  Each lane's 8 k values
+//     x and B = 32 k x 16 rows of decoded weights (a 32-token pass feeds each
+//     decoded B to two A tiles).  Each lane's 8 k values
 //     are 8 consecutive columns; the weight bytes are put into that order
 //     with v_perm_b32, which also ORs in the fp16 exponent;
 //   * B holds exact integers wherever the format allows (Hitchhiker's Guide
@@ -165,18 +166,30 @@ __device__ __forceinline__ uint32_t bits_to_b4(uint32_t v4) {
   return (((v4 & 0xFu) * 0x00204081u) & 0x01010101u) << 4;   // a 24-bit multiply
 }
 
-// P += A(chunk k) x B, with fp32 activations as hi + lo.
+// 16-token matrix-op tiles per pass: one for P = 8 or 16, two for P = 32
+// (each decoded B fragment then feeds both tiles).
+template <int P> constexpr int kMT = P > 16 ? P / 16 : 1;
+
+// P[mt] += A(tile mt, chunk k) x B, with fp32 activations as hi + lo.
 template <bool XLO, int P>
-__device__ __forceinline__ void mma(const uint8_t* xw, int t, int k, f16x8 B, f32x4v& Pc) {
-  Pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a<P>(xw, t, k), B, Pc, 0, 0, 0);
-  if constexpr (XLO) Pc = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a<P>(xw + P * 512, t, k), B, Pc, 0, 0, 0);
+__device__ __forceinline__ void mma(const uint8_t* xw, int t, int k, f16x8 B, f32x4v (&Pc)[kMT<P>]) {
+#pragma unroll
+  for (int mt = 0; mt < kMT<P>; mt++) {
+    Pc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a<P>(xw, t + 16 * mt, k), B, Pc[mt], 0, 0, 0);
+    if constexpr (XLO)
+      Pc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(read_a<P>(xw + P * 512, t + 16 * mt, k), B,
+                                                      Pc[mt], 0, 0, 0);
+  }
 }
 
-// acc += the slab's contribution for this wave's 16 rows x 16 tokens.
+// acc[mt] += the slab's contribution for this wave's 16 rows x tokens
+// 16 mt .. 16 mt + 15 of the pass.
 // Activation chunk of MFMA step j for lane group g: K-quant lanes own columns
 // 64 g .. 64 g + 63 (their two sub-blocks), 32-weight types 32 j + 8 g.
 template <int T, bool XLO, int P>
-__device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& ws, int g, f32x4v& acc) {
+__device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& ws, int g,
+                                         f32x4v (&acc)[kMT<P>]) {
+  constexpr int MT = kMT<P>;
   const f32x4v z = {0.f, 0.f, 0.f, 0.f};
   if constexpr (T == GQ_Q4_K) {
     const float d = h2f(ws.hd.x), dmin = h2f(ws.hd.x >> 16);
@@ -193,7 +206,9 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
       const _Float16 mh = (_Float16)m;
       M[h] = f16x8{mh, mh, mh, mh, mh, mh, mh, mh};
     }
-    f32x4v Pk = z, Pm = z;
+    f32x4v Pk[MT], Pm[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) Pk[mt] = Pm[mt] = z;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       const int h = j >> 2, qq = j & 3;       // sub-block 2g + h, eighth qq
@@ -204,20 +219,28 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
       const f16x2 s = (qq < 2) ? SL[h] : SH[h], n = (qq < 2) ? NL[h] : NH[h];
       const f16x8 B = cat8(__builtin_elementwise_fma(v[0], s, n), __builtin_elementwise_fma(v[1], s, n),
                            __builtin_elementwise_fma(v[2], s, n), __builtin_elementwise_fma(v[3], s, n));
-      const f16x8 ah = read_a<P>(xw, t, 8 * g + j);
-      Pk = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, B, Pk, 0, 0, 0);
-      Pm = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, M[h], Pm, 0, 0, 0);
-      if constexpr (XLO) {
-        const f16x8 al = read_a<P>(xw + P * 512, t, 8 * g + j);
-        Pk = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, B, Pk, 0, 0, 0);
-        Pm = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, M[h], Pm, 0, 0, 0);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const f16x8 ah = read_a<P>(xw, t + 16 * mt, 8 * g + j);
+        Pk[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, B, Pk[mt], 0, 0, 0);
+        Pm[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, M[h], Pm[mt], 0, 0, 0);
+        if constexpr (XLO) {
+          const f16x8 al = read_a<P>(xw + P * 512, t + 16 * mt, 8 * g + j);
+          Pk[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, B, Pk[mt], 0, 0, 0);
+          Pm[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, M[h], Pm[mt], 0, 0, 0);
+        }
       }
     }
-    acc += d * Pk;
-    acc -= dmin * Pm;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      acc[mt] += d * Pk[mt];
+      acc[mt] -= dmin * Pm[mt];
+    }
   } else if constexpr (T == GQ_Q6_K) {
     const float d = h2f(ws.d);
-    f32x4v Pk = z;
+    f32x4v Pk[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) Pk[mt] = z;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       const int h = j >> 2, qq = j & 3;       // 32-group 2g + h, eighth qq
@@ -234,7 +257,8 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
                            __builtin_elementwise_fma(v[2], s, n), __builtin_elementwise_fma(v[3], s, n));
       mma<XLO, P>(xw, t, 8 * g + j, B, Pk);
     }
-    acc += d * Pk;
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[mt] += d * Pk[mt];
   } else {
     const f16x2 off = (T == GQ_Q8_0) ? hpair(-1152.f, -1152.f)
                       : (T == GQ_Q5_0) ? hpair(-1040.f, -1040.f) : hpair(-1032.f, -1032.f);
@@ -257,9 +281,13 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
       f16x2 v[4];
       bytes8(kE1024, c0, c1, v);
       const f16x8 B = cat8(v[0] + off, v[1] + off, v[2] + off, v[3] + off);
-      f32x4v Pk = z;
+      f32x4v Pk[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) Pk[mt] = z;
       mma<XLO, P>(xw, t, 4 * j + g, B, Pk);
-      acc += h2f(ws.d[j]) * Pk;
+      const float dj = h2f(ws.d[j]);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] += dj * Pk[mt];
     }
   }
 }
@@ -322,7 +350,10 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
   };
 
   const int cnt = (nslab - 1 - w) / KS + 1;   // this wave's slabs (w < KS <= nslab)
-  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  constexpr int MT = kMT<P>;
+  f32x4v acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
   XS<XLO, P> xs[D];
   WS<T> ws[D];
 #pragma unroll
@@ -351,25 +382,29 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
     m0 += D;
   } while (m0 < cnt);
 
-  // D lane l holds rows (tokens) 4(l/16) + v of column (weight row) l % 16
+  // D lane l of tile mt holds rows (tokens) 16 mt + 4(l/16) + v of column
+  // (weight row) l % 16
   if (KS == 1) {
 #pragma unroll
-    for (int v = 0; v < 4; v++) {
-      const int t = 4 * g + v;
-      if (t < nt && r < nr) y[(int64_t)(tok0 + t) * rows + row0 + r] = acc[v];
-    }
+    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int t = 16 * mt + 4 * g + v;
+        if (t < nt && r < nr) y[(int64_t)(tok0 + t) * rows + row0 + r] = acc[mt][v];
+      }
     return;
   }
   __syncthreads();                            // every wave is done with its block
-  f32x4v* red = reinterpret_cast<f32x4v*>(lds);   // [KS][64]
-  red[w * 64 + lane] = acc;
+  f32x4v* red = reinterpret_cast<f32x4v*>(lds);   // [KS][MT][64]
+#pragma unroll
+  for (int mt = 0; mt < MT; mt++) red[(w * MT + mt) * 64 + lane] = acc[mt];
   __syncthreads();
-  for (int o = threadIdx.x; o < 256; o += blockDim.x) {
-    const int t = o >> 4, rr = o & 15;
+  for (int o = threadIdx.x; o < 256 * MT; o += blockDim.x) {
+    const int mt = o >> 8, t = (o >> 4) & 15, rr = o & 15;
     const int src = 16 * (t >> 2) + rr, v = t & 3;
     float sum = 0.f;
-    for (int k = 0; k < KS; k++) sum += red[k * 64 + src][v];
-    if (t < nt && rr < nr) y[(int64_t)(tok0 + t) * rows + row0 + rr] = sum;
+    for (int k = 0; k < KS; k++) sum += red[(k * MT + mt) * 64 + src][v];
+    if (16 * mt + t < nt && rr < nr) y[(int64_t)(tok0 + 16 * mt + t) * rows + row0 + rr] = sum;
   }
 }
 
@@ -394,6 +429,12 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #ifndef GQ_MMV_WAVES
 #define GQ_MMV_WAVES 4096                     // target waves per launch
 #endif
+#ifndef GQ_MMV_DEPTH32                        // ring depth of the 32-token passes
+#define GQ_MMV_DEPTH32 1
+#endif
+#ifndef GQ_MMV_P32_FROM                      // fp16 x: passes of 32 tokens above this many
+#define GQ_MMV_P32_FROM 16
+#endif
 #ifndef GQ_MMV_DEPTH
 #define GQ_MMV_DEPTH 2                        // ring depth with fp16 activations
 #endif
@@ -415,7 +456,8 @@ template <int T, bool XLO, int P>
 hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
                  hipStream_t st) {
   // ring depth: as deep as the registers allow without spilling
-  constexpr int D = XLO ? (P == 8 ? 2 : 1) : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
+  constexpr int D = XLO ? (P == 8 ? 2 : 1) : (P == 32) ? GQ_MMV_DEPTH32
+                   : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
   return mmv_launch<T, XLO, P, D>(blob, rows, cols, x, n, y,
                                   pick_ks(rows, cols, n, P, P * 512 * (XLO ? 2 : 1)), st);
 }
@@ -423,8 +465,16 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
 template <int T, bool XLO>
 hipError_t mmv_t(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
                  hipStream_t st) {
-  return n <= 8 ? mmv_p<T, XLO, 8>(blob, rows, cols, x, n, y, st)
-                : mmv_p<T, XLO, 16>(blob, rows, cols, x, n, y, st);
+  if (n <= 8) return mmv_p<T, XLO, 8>(blob, rows, cols, x, n, y, st);
+  // 32-token passes (fp16 x) halve the decode work per token, which is what
+  // bounds the 32-weight types and Q6_K; they need at least 256 workgroups
+  // (16-row tiles x passes) to cover the chip, and for Q4_K, whose decode is
+  // cheap, they only pay up to 512 row tiles (measured on MI355X).
+  const int64_t tiles = (rows + 15) / 16, passes32 = (n + 31) / 32;
+  const bool p32 = !XLO && n > GQ_MMV_P32_FROM && tiles * passes32 >= 256 &&
+                   (T != GQ_Q4_K || tiles <= 512);
+  if (!p32) return mmv_p<T, XLO, 16>(blob, rows, cols, x, n, y, st);
+  return mmv_p<T, false, 32>(blob, rows, cols, x, n, y, st);
 }
 
 }  // namespace
