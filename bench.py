@@ -184,7 +184,7 @@ def replay_spread(graphs, n, per_graph):
 
 def stream_read_reference(steps):
     """Achieved bandwidth of the library's plain streaming-read kernel
-    (gq_probe_stream_read: 128-bit loads, every byte once) at the dominant
+    (gq_probe_stream_read: non-temporal 128-bit loads, every byte once) at the dominant
     launch's size and at 1 GiB, rotating over copies totalling >= 2x the
     Infinity Cache: the practical ceiling the GEMV's fraction of the nominal
     peak is read against."""
@@ -209,7 +209,8 @@ def stream_read_reference(steps):
         out[label] = round(nbytes / (ms * 1e-3) / 1e9, 1)
         del bufs, graphs
         torch.cuda.empty_cache()
-    return {"kernel": "gq_probe_stream_read (128-bit loads, each byte once)", "GBps": out}
+    return {"kernel": "gq_probe_stream_read (non-temporal 128-bit loads, each byte once)",
+            "GBps": out}
 
 
 def kernel_time_ms(mat, steps, per_graph=16, spread=False):

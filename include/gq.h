@@ -231,7 +231,7 @@ int gq_attn_decode(const void *k_cache, const void *v_cache, int kv_type, int64_
 
 /*
  * Measurement: a plain streaming read of `bytes` bytes of device memory at
- * buf with 128-bit loads, every byte read once, nothing else done.  Its
+ * buf with non-temporal 128-bit loads, every byte read once, nothing else done.  Its
  * bandwidth is the practical ceiling the GEMV kernels' effective bandwidth
  * is read against (no kernel reaches the nominal HBM peak).  So that the
  * reads cannot be dropped, out (device, GQ_PROBE_OUT_WORDS 32-bit words,
