@@ -303,6 +303,33 @@ def cpu_baseline(layer_mats):
     }
 
 
+def cpu_baseline_gemm(threads=None):
+    """The CPU oracle on the 512-token GEMM workload: Q4_K weights drawn as
+    the bench draws them (N(0, 0.02^2), quantized by the oracle) times 512
+    fp16 N(0, 1) tokens, on a sample of 688 rows (1/16 of the 11008-row
+    matrix, all 512 tokens), repeated for about 8 s on all threads;
+    GFLOP/s = 2 * rows * cols * 512 / time."""
+    import numpy as np
+    import oracle
+    import synth
+    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    rows, cols, n = 688, 4096, 512
+    w = synth.weights(rows, cols, seed=9000)
+    blob = oracle.quantize(w, "q4_k")
+    x = synth.activations(n, cols, seed=9100, dtype="f16")
+    ts = []
+    t_start = time.perf_counter()
+    while len(ts) < 3 or time.perf_counter() - t_start < 8.0:
+        t0 = time.perf_counter()
+        oracle.matmul_f64(blob, "q4_k", rows, cols, x, threads=threads)
+        ts.append(time.perf_counter() - t0)
+    t = float(np.median(ts))
+    return {"value": round(2.0 * rows * cols * n / t / 1e9, 2), "unit": "GFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} of the 11008 rows x 4096 columns, all {n} fp16 tokens, fp64 "
+                      f"dequant-then-dot, median of {len(ts)} repetitions ({t:.2f} s each)"}
+
+
 def sweep(steps):
     """Secondary shapes: one line each, graph-timed with rotating copies."""
     import synth
@@ -547,6 +574,9 @@ def main():
                                   "traffic": gemm_fetch_from_profile(),
                                   "traffic_note": "HBM bytes fetched per launch (FETCH_SIZE, "
                                                   "calibrated); writes not included"}}
+        if not args.no_cpu:
+            log("cpu baseline of the 512-token GEMM (oracle)")
+            secondary["cpu_baseline"] = cpu_baseline_gemm()
 
     attn = None
     if not args.no_sweep:
