@@ -14,8 +14,10 @@
 //     swizzled per slice) with the sums of x over every 16 columns;
 //   * Q4_K and Q6_K use factored sub-block sums a*sum(q*x) - b*sum(x)
 //     (Hitchhiker's Guide §11.2, w = (d*sc)*q - dmin*m; for Q6_K the offset
-//     32 plays the min); the 32-weight types convert each code to the signed
-//     q - offset so every product is exact relative to w; fp32 accumulation;
+//     32 plays the min), Q4_K codes entering their products as fp16
+//     subnormals (one mixed-precision FMA per weight, no convert); the
+//     32-weight types convert each code to the signed q - offset so every
+//     product is exact relative to w; fp32 accumulation;
 //   * persistent workgroups (as many as fit on the chip) loop over groups of
 //     rows with the next group's loads in flight (a wave's first two items
 //     go out before or after x is staged, by how many items it has); row
@@ -25,13 +27,7 @@
 
 namespace gq {
 
-// acc + sum over the 4 bytes of w (as unsigned / signed integers) * x[k].
-__device__ __forceinline__ float dot4u(uint32_t w, const float* x, float acc) {
-  acc = fmaf(ub0(w), x[0], acc);
-  acc = fmaf(ub1(w), x[1], acc);
-  acc = fmaf(ub2(w), x[2], acc);
-  return fmaf(ub3(w), x[3], acc);
-}
+// acc + sum over the 4 bytes of w (as signed integers) * x[k].
 __device__ __forceinline__ float dot4s(uint32_t w, const float* x, float acc) {
   acc = fmaf(sb0(w), x[0], acc);
   acc = fmaf(sb1(w), x[1], acc);
@@ -39,11 +35,11 @@ __device__ __forceinline__ float dot4s(uint32_t w, const float* x, float acc) {
   return fmaf(sb3(w), x[3], acc);
 }
 
-// The same as dot4u / dot4s with each byte's convert and its FMA kept
-// adjacent in one asm block: the scheduler cannot hoist a whole slice's
-// converts ahead of the FMAs and hold 64 converted codes live at once (Q6_K's
-// decode, or any type's with two row sets, otherwise needs enough registers
-// to halve the waves per SIMD).
+// dot4s, and the same over unsigned bytes, with each byte's convert and its
+// FMA kept adjacent in one asm block: the scheduler cannot hoist a whole
+// slice's converts ahead of the FMAs and hold 64 converted codes live at once
+// (Q6_K's decode, or any type's with two row sets, otherwise needs enough
+// registers to halve the waves per SIMD).
 __device__ __forceinline__ float dot4u_asm(uint32_t w, const float* x, float acc) {
   float t;
   asm("v_cvt_f32_ubyte0 %1, %2\n\tv_fmac_f32 %0, %1, %3\n\t"
@@ -68,14 +64,28 @@ __device__ __forceinline__ float dot4s_asm(uint32_t w, const float* x, float acc
       : "v"(w), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
   return acc;
 }
-template <bool ASM>
-__device__ __forceinline__ float dot4u_(uint32_t w, const float* x, float acc) {
-  return ASM ? dot4u_asm(w, x, acc) : dot4u(w, x, acc);
-}
+
 template <bool ASM>
 __device__ __forceinline__ float dot4s_(uint32_t w, const float* x, float acc) {
   return ASM ? dot4s_asm(w, x, acc) : dot4s(w, x, acc);
 }
+
+// acc + 2^-24 (c0 x[0] + c1 x[1] + c2 x[2] + c3 x[3]) for unsigned codes c_i
+// held in 16-bit fields, c0 and c2 in the low and high field of p02, c1 and c3
+// in those of p13.  A field below 1024 read as fp16 is the subnormal c * 2^-24
+// exactly, so each v_fma_mix_f32 takes a code straight to its fp32 product
+// with x: the sum is exactly 2^-24 times the one convert + FMA gives, with the
+// same roundings, while x * 2^-24 stays a normal fp32 number (|x| > 2^-102).
+__device__ __forceinline__ float dot4mix(uint32_t p02, uint32_t p13, const float* x, float acc) {
+  asm("v_fma_mix_f32 %0, %1, %3, %0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %0, %2, %4, %0 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %0, %1, %5, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %0, %2, %6, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(acc)
+      : "v"(p02), "v"(p13), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+  return acc;
+}
+constexpr float kSub = 16777216.f;            // 2^24: undoes the subnormal scale
 
 // One lane's 64-weight slice of one row: raw registers and the slice dot in
 // two halves of 32 weights.  voff(sl) is slice sl's byte offset in its row;
@@ -99,17 +109,18 @@ template <> struct Slice<GQ_Q4_K> {           // sub-blocks 2j, 2j+1 of a super-
     float s = 0.f, t = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; k++) {             // low nibbles: elements 4k.., high: 16+4k..
-      s = dot4u_<ASM>(q[k] & 0x0F0F0F0Fu, x + 4 * k, s);
-      t = dot4u_<ASM>((q[k] >> 4) & 0x0F0F0F0Fu, x + 16 + 4 * k, t);
+      const uint32_t u = q[k] >> 8;           // high nibbles stay in place: 16 q
+      s = dot4mix(q[k] & 0x000F000Fu, u & 0x000F000Fu, x + 4 * k, s);
+      t = dot4mix(q[k] & 0x00F000F0u, u & 0x00F000F0u, x + 16 + 4 * k, t);
     }
     // (scale, min) of sub-blocks 2j, 2j+1: the 24 bits at bit 24j of the
     // 96-bit field stream in header bytes 4..15
     const uint32_t lo = (j <= 1) ? hd.y : (j == 2) ? hd.z : hd.w;
     const uint32_t hi = (j <= 1) ? hd.z : hd.w;
     const uint32_t f = __builtin_amdgcn_alignbit(hi, lo, (24 * j) & 31) >> (12 * h);
-    const float a = h2f(hd.x) * (float)(f & 63u);
+    const float a = h2f(hd.x) * (float)(f & 63u) * kSub;
     const float b = h2f(hd.x >> 16) * (float)((f >> 6) & 63u);
-    return fmaf(a, s + t, -b * (xs[0] + xs[1]));
+    return fmaf(a, fmaf(t, 0.0625f, s), -b * (xs[0] + xs[1]));
   }
 };
 
@@ -223,10 +234,12 @@ __device__ __forceinline__ int xswz(int f) {
 // (one more barrier, for the sum of squares); F_GLU reads a second matrix of
 // the same shape (row set 1 from blob2, the same rows as row set 0 from
 // blob) and stores silu(row set 0) * row set 1.
+// A workgroup has W waves sharing one copy of x (W = 8 for long rows, where
+// x's LDS would otherwise cap the resident waves below what registers allow).
 constexpr int F_NORM = 1, F_GLU = 2;
 
-template <int T, bool XF16, int LPR, int R, int XPT, bool XFIRST, int F = 0>
-__global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, int rows,
+template <int T, bool XF16, int LPR, int R, int XPT, bool XFIRST, int F = 0, int W = 4>
+__global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blob, int rows,
                                               int cols, int rb, const void* __restrict__ xv,
                                               float* __restrict__ y,
                                               const uint8_t* __restrict__ blob2 = nullptr,
@@ -237,14 +250,14 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   static_assert(!GLU || R == 2, "the gated form takes two row sets");
   constexpr int RPW = 64 / LPR;            // rows side by side in a wave
   constexpr int ROWS = GLU ? RPW : RPW * R;   // rows per group
-  // XPT = float4 of x staged per thread: cols <= XPT * 1024
+  // XPT = float4 of x staged per thread: cols <= XPT * 256 * W
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int nsl = (cols + 63) >> 6;        // slices per row (the last may be half)
   const int npass = (nsl + LPR - 1) / LPR;
   const int cpad = nsl << 6;
   const int ngroups = (rows + ROWS - 1) / ROWS;
-  const int stride = gridDim.x * 4;
+  const int stride = gridDim.x * W;
   const int sub = lane / LPR;              // which of the side-by-side rows
   const int li = lane % LPR;
 
@@ -254,7 +267,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   f32x4 xr[XPT], gr[NORM ? XPT : 1];
 #pragma unroll
   for (int i = 0; i < XPT; i++) {
-    const int cc = min((int)threadIdx.x + 256 * i, nc4 - 1);
+    const int cc = min((int)threadIdx.x + 64 * W * i, nc4 - 1);
     if constexpr (XF16) {
       u32x2 hh = *reinterpret_cast<const u32x2*>((const _Float16*)xv + 4 * cc);
       xr[i] = f32x4{h2f(hh.x), h2f(hh.x >> 16), h2f(hh.y), h2f(hh.y >> 16)};
@@ -284,8 +297,8 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   // first, are the only ones the staging waits for), after it when they
   // have few (x then reaches every CU ahead of the weight traffic, and the
   // kernel's span is the x latency plus one or two items' work).
-  int g = blockIdx.x * 4 + wave;
-  Slice<T> nxt[R];
+  int g = blockIdx.x * W + wave;
+  Slice<T> nxt[R] = {};
   auto first_two = [&]() {
     if (g < ngroups) load_item(cur, g, 0);
     if (g < ngroups && (npass > 1 || g + stride < ngroups)) {
@@ -298,21 +311,23 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   // RMSNorm ("How LLM Inference Engines Work", "RMSNorm"): s = rsqrt(mean(x^2)
   // + eps) in fp32, x' = (x * s rounded to x's type) * gamma.  Every
   // workgroup forms the sum of squares itself: per thread, then the DPP
-  // network, then the four waves in order through LDS.
+  // network, then the W waves in order through LDS.
   float* xsum = xsm + cpad;
   if constexpr (NORM) {
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < XPT; i++) {
-      const int c4 = (int)threadIdx.x + 256 * i;
+      const int c4 = (int)threadIdx.x + 64 * W * i;
       const f32x4 v = (c4 < nc4) ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
       q += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
     }
     q = group_sum_dpp<64>(q);                // the wave's total in lane 63
-    float* const part = xsum + (cpad >> 4);  // 4 floats after the column sums
+    float* const part = xsum + (cpad >> 4);  // W floats after the column sums
     if (lane == 63) part[wave] = q;
     __syncthreads();
-    const float tot = (part[0] + part[1]) + (part[2] + part[3]);
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; i += 4) tot += (part[i] + part[i + 1]) + (part[i + 2] + part[i + 3]);
     const float sc = 1.f / sqrtf(tot / (float)cols + eps);
 #pragma unroll
     for (int i = 0; i < XPT; i++) {
@@ -328,7 +343,7 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
   // one 16-column group, summed on the DPP network
 #pragma unroll
   for (int i = 0; i < XPT; i++) {
-    const int c4 = (int)threadIdx.x + 256 * i;
+    const int c4 = (int)threadIdx.x + 64 * W * i;
     const f32x4 v = (c4 < nc4) ? xr[i] : f32x4{0.f, 0.f, 0.f, 0.f};
     float s = (v.x + v.y) + (v.z + v.w);
     s += dpp_mov<0xB1>(s);
@@ -377,10 +392,9 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
           acc[k] += use ? d : 0.f;
         }
       }
-      if (more) {
+      // unconditional: without a next item the loops end here and cur is dead
 #pragma unroll
-        for (int k = 0; k < R; k++) cur[k] = nxt[k];
-      }
+      for (int k = 0; k < R; k++) cur[k] = nxt[k];
     }
     if constexpr (GLU) {
       // SwiGLU ("How LLM Inference Engines Work", "SwiGLU Feed-Forward
@@ -402,9 +416,15 @@ __global__ void __launch_bounds__(256) k_gemv(const uint8_t* __restrict__ blob, 
 #ifndef GQ_GEMV_R                 // row sets per wave when a row takes one pass
 #define GQ_GEMV_R 1
 #endif
+#ifndef GQ_GEMV_W                 // waves per workgroup for rows of up to 8192
+#define GQ_GEMV_W 4
+#endif
+#ifndef GQ_GEMV_LONG_W            // waves per workgroup for longer rows
+#define GQ_GEMV_LONG_W 8
+#endif
 
 template <typename K>
-static int resident_wgs(K kern, size_t lds) {
+static int resident_wgs(K kern, int threads, size_t lds) {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
@@ -413,7 +433,7 @@ static int resident_wgs(K kern, size_t lds) {
       cus = 256;
   }
   int per = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)kern, 256, lds) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)kern, threads, lds) != hipSuccess ||
       per < 1)
     per = 1;
   return cus * per;
@@ -426,47 +446,51 @@ struct Fuse {
   float eps;
 };
 
-template <int T, bool XF16, int LPR, int R, int XPT, int F>
+template <int T, bool XF16, int LPR, int R, int XPT, int F, int W = 4>
 static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, const void* x,
                               float* y, const Fuse& fu, hipStream_t st) {
   constexpr int RR = (F & F_GLU) ? 2 : R;
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t cpad = (cols + 63) / 64 * 64;
-  // x, its 16-column sums and 4 per-wave partial sums: <= 68 KB for cols <= 16384
-  const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4 + 16;
-  auto kern = k_gemv<T, XF16, LPR, RR, XPT, false, F>;
+  // x, its 16-column sums and W per-wave partial sums: <= 68 KB for cols <= 16384
+  const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4 + 4 * W;
+  auto kern = k_gemv<T, XF16, LPR, RR, XPT, false, F, W>;
   static size_t cap_lds = 0;               // resident workgroups for the last LDS size
   static int cap = 0;                      // (both orders use the same registers)
-  if (cap_lds != lds) { cap = resident_wgs(kern, lds); cap_lds = lds; }
+  if (cap_lds != lds) { cap = resident_wgs(kern, 64 * W, lds); cap_lds = lds; }
   const int64_t rpg = (F & F_GLU) ? (64 / LPR) : (64 / LPR) * RR;   // rows per group
   const int64_t groups = (rows + rpg - 1) / rpg;
-  const int64_t wgs = (groups + 3) / 4;
+  const int64_t wgs = (groups + W - 1) / W;
   dim3 grid((unsigned)(wgs < cap ? wgs : cap));
   // items of the wave with the most: x goes first when that is at most 2
   const int64_t npass = ((cols + 63) / 64 + LPR - 1) / LPR;
-  const int64_t most = (groups + 4 * (int64_t)grid.x - 1) / (4 * (int64_t)grid.x) * npass;
+  const int64_t most = (groups + W * (int64_t)grid.x - 1) / (W * (int64_t)grid.x) * npass;
   const uint8_t* b2 = (const uint8_t*)fu.blob2;
   if (most <= 2)
-    hipLaunchKernelGGL((k_gemv<T, XF16, LPR, RR, XPT, true, F>), grid, dim3(256), lds, st,
+    hipLaunchKernelGGL((k_gemv<T, XF16, LPR, RR, XPT, true, F, W>), grid, dim3(64 * W), lds, st,
                        (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, y, b2, fu.gamma,
                        fu.eps);
   else
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, (const uint8_t*)blob, (int)rows,
+    hipLaunchKernelGGL(kern, grid, dim3(64 * W), lds, st, (const uint8_t*)blob, (int)rows,
                        (int)cols, (int)rb, x, y, b2, fu.gamma, fu.eps);
   return hipGetLastError();
 }
 
 // Shape dispatch: rows of up to 2048 weights share a wave (64/LPR of them);
 // longer rows take several passes of 64 slices.  Rows of up to 4096 weights
-// take R row sets per wave, longer ones one.
+// take R row sets per wave, longer ones one.  Rows of more than 8192 weights
+// take 8-wave workgroups: with 4, x's LDS (> 32 KB) leaves fewer waves
+// resident than registers allow, and e.g. 4096 rows then spread unevenly
+// (some waves two rows, some one).
 template <int T, bool XF16, int F>
 static hipError_t gemv_pick(const void* blob, int64_t rows, int64_t cols, const void* x, float* y,
                             const Fuse& fu, hipStream_t st) {
-  if (cols <= 1024) return gemv_launch<T, XF16, 16, GQ_GEMV_R, 4, F>(blob, rows, cols, x, y, fu, st);
-  if (cols <= 2048) return gemv_launch<T, XF16, 32, GQ_GEMV_R, 4, F>(blob, rows, cols, x, y, fu, st);
-  if (cols <= 4096) return gemv_launch<T, XF16, 64, GQ_GEMV_R, 4, F>(blob, rows, cols, x, y, fu, st);
-  if (cols <= 8192) return gemv_launch<T, XF16, 64, 1, 8, F>(blob, rows, cols, x, y, fu, st);
-  return gemv_launch<T, XF16, 64, 1, 16, F>(blob, rows, cols, x, y, fu, st);
+  constexpr int W = GQ_GEMV_W, LW = GQ_GEMV_LONG_W;
+  if (cols <= 1024) return gemv_launch<T, XF16, 16, GQ_GEMV_R, 16 / W, F, W>(blob, rows, cols, x, y, fu, st);
+  if (cols <= 2048) return gemv_launch<T, XF16, 32, GQ_GEMV_R, 16 / W, F, W>(blob, rows, cols, x, y, fu, st);
+  if (cols <= 4096) return gemv_launch<T, XF16, 64, GQ_GEMV_R, 16 / W, F, W>(blob, rows, cols, x, y, fu, st);
+  if (cols <= 8192) return gemv_launch<T, XF16, 64, 1, 32 / W, F, W>(blob, rows, cols, x, y, fu, st);
+  return gemv_launch<T, XF16, 64, 1, 64 / LW, F, LW>(blob, rows, cols, x, y, fu, st);
 }
 
 template <int T, int F>
