@@ -9,7 +9,8 @@
 //     w = (d*sc)*q - dmin*m), i.e. exactly the fp16 output of gq_dequant:
 //     every weight is decoded with one fp32 fma and rounded to fp16 by
 //     v_fma_mix (relative error <= 2^-11 per weight, inside the stated
-//     1e-3 of sum |w*x|);
+//     1e-3 of sum |w*x|); Q4_K codes reach it as fp16 subnormals, so they
+//     need no convert;
 //   * workgroup tile 128 tokens x 256 weight rows, K steps of 64 columns;
 //     8 waves, each owning 32 weight rows x all 128 tokens (4 x 1
 //     v_mfma_f32_32x32x16_f16 per 16 columns);
@@ -60,6 +61,25 @@ __device__ __forceinline__ uint32_t h2pack(float a, float b) {
   return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
 }
 
+// fp16 pair {RNE_fp16(c0 s + nb), RNE_fp16(c1 s + nb)} for codes held in
+// 16-bit fields (c0 in field H of p0, c1 in field H of p1) and a scale s
+// carrying a factor 2^24: a field below 1024 read as fp16 is the subnormal
+// c * 2^-24 exactly, so each v_fma_mix forms the exact c * (s 2^-24) + nb and
+// rounds it once, as the convert-then-mix form does, with no convert.
+template <int H>
+__device__ __forceinline__ uint32_t mixpair(uint32_t p0, uint32_t p1, float s, float nb) {
+  uint32_t d;
+  if constexpr (H == 0)
+    asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel_hi:[1,0,0]"
+        : "=&v"(d) : "v"(p0), "v"(p1), "v"(s), "v"(nb));
+  else
+    asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(d) : "v"(p0), "v"(p1), "v"(s), "v"(nb));
+  return d;
+}
+
 // ---------------------------------------------------------------------------
 // Weights.  Thread (row r, half h) owns 32 columns of its row per K step: the
 // "segment" sg = 2 * step + h (one Q4_K sub-block, one Q6_K group of 32, one
@@ -80,16 +100,17 @@ template <> struct BR<GQ_Q4_K> {
     const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
     const uint32_t f = q4k_pair(hd.y, hd.z, hd.w, sg & 7);
     const float a = d * (float)(f & 63u), nb = -(dmin * (float)(f >> 6));
-    const float a16 = a * 0.0625f;           // high nibbles enter as 16 q
+    // codes enter as fp16 subnormals q * 2^-24 (high nibbles in place: 16 q)
+    const float a24 = a * 16777216.f, a20 = a * 1048576.f;
 #pragma unroll
     for (int c = 0; c < 4; c++) {            // chunk c: elements 8c .. 8c+7
-      const uint32_t m = (c < 2) ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
-      const float s = (c < 2) ? a : a16;
-      const uint32_t v0 = q[2 * (c & 1)] & m, v1 = q[2 * (c & 1) + 1] & m;
-      out[c] = u32x4{h2pack(fmaf(ub0(v0), s, nb), fmaf(ub1(v0), s, nb)),
-                     h2pack(fmaf(ub2(v0), s, nb), fmaf(ub3(v0), s, nb)),
-                     h2pack(fmaf(ub0(v1), s, nb), fmaf(ub1(v1), s, nb)),
-                     h2pack(fmaf(ub2(v1), s, nb), fmaf(ub3(v1), s, nb))};
+      const uint32_t m = (c < 2) ? 0x000F000Fu : 0x00F000F0u;
+      const float s = (c < 2) ? a24 : a20;
+      const uint32_t w0 = q[2 * (c & 1)], w1 = q[2 * (c & 1) + 1];
+      const uint32_t e0 = w0 & m, o0 = (w0 >> 8) & m;   // bytes 0, 2 / 1, 3 of w0
+      const uint32_t e1 = w1 & m, o1 = (w1 >> 8) & m;
+      out[c] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
+                     mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
     }
   }
 };
@@ -197,8 +218,10 @@ template <bool XLO, int NT> struct AR {
 
 }  // namespace
 
+// VALU instructions placed after each MFMA (measured best: 5, Q6_K's heavier
+// decode 3)
 #ifndef GQ_GEMM_VPM
-#define GQ_GEMM_VPM 5                         // VALU instructions placed after each MFMA
+#define GQ_GEMM_VPM (T == GQ_Q6_K ? 3 : 5)
 #endif
 
 template <int T, bool XLO, int D>
