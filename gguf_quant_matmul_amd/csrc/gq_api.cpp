@@ -14,7 +14,8 @@ constexpr int64_t kBytes = (int64_t)1 << 47;     // any one buffer < 2^47 bytes
 constexpr int64_t kMaxColsGemv = 16384;          // x staged in 64 KB of LDS
 constexpr int64_t kMaxColsBatch = (int64_t)1 << 21;  // n_tok >= 2: 128 tokens of x in 31-bit offsets
 constexpr int64_t kMaxTokens = (int64_t)1 << 22;  // matrix-core grid.y = n_tok / 64 < 65536
-constexpr int64_t kSmallBatch = 64;               // n_tok up to this: weight-stream kernel
+constexpr int64_t kSmallBatch = 64;               // tokens per weight-stream launch at most
+constexpr int64_t kStreamOnly = 32;               // n_tok up to this: always the weight stream
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // dequant / quantize grid.x < 2^31
 
 bool quant_type(int t) { return t >= GQ_Q4_0 && t <= GQ_Q6_K; }
@@ -39,19 +40,16 @@ int check_matrix(int type, int64_t rows, int64_t cols, int64_t* rb) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_EHIP; }
 
-// Past 64 tokens: the matrix-core GEMM walks every tile's whole K range, so
-// its time is ~ K steps x step time whenever its tiles (256 rows x 128
-// tokens) leave CUs idle, while the weight-stream kernel's time grows with
-// the number of 16-token passes.  Measured on MI355X: a K step takes ~1.0 us
-// (1.8 us for Q6_K) and a 16-token pass of the weight-stream kernel streams
-// rows*cols weights at ~150 (Q6_K ~118) TFLOP/s.  The batch goes to the
-// weight-stream kernel in ceil(n/64) near-equal chunks (each of 33 to 64
-// tokens) when that estimate is lower.
+// Past 32 tokens: the matrix-core GEMM walks every tile's whole K range, so
+// its time is ~ rounds of resident tiles x K steps x step time (its own
+// estimate, by tile shape), while the weight-stream kernel's time grows with
+// the number of 16-token passes: measured on MI355X, a pass streams
+// rows*cols weights at ~150 (Q6_K ~165, the 32-weight types ~65) TFLOP/s.  The batch goes to the
+// weight-stream kernel, in ceil(n/64) near-equal chunks of at most 64 tokens,
+// when that estimate is lower.
 bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_tok) {
-  const double step_us = (type == GQ_Q6_K) ? 1.8 : 1.0;
-  const double rate = (type == GQ_Q6_K) ? 118e12 : 150e12;
-  const int64_t tiles = (rows + 255) / 256 * ((n_tok + 127) / 128);
-  const double gemm_us = (double)((tiles + 255) / 256) * (double)((cols + 63) / 64) * step_us;
+  const double rate = (type == GQ_Q4_K) ? 150e12 : (type == GQ_Q6_K) ? 165e12 : 65e12;
+  const double gemm_us = gq::gemm_estimate_us(type, rows, cols, n_tok);
   const double pass_us = (double)rows * (double)cols * 32.0 / rate * 1e6;
   const int64_t k = (n_tok + 63) / 64, base = n_tok / k, extra = n_tok % k;
   const int64_t passes = extra * ((base + 16) / 16) + (k - extra) * ((base + 15) / 16);
@@ -130,7 +128,7 @@ int gq_matmul_path(const void* weight_blob, int ggml_type, int64_t rows, int64_t
   const bool xf16 = (x_type == GQ_F16);
   if (n_tok == 1) return hip_status(gq::launch_gemv(ggml_type, weight_blob, rows, cols, x, xf16, y, st));
   if (path == GQ_PATH_AUTO)
-    path = (n_tok <= kSmallBatch || small_batch_chunks_faster(ggml_type, rows, cols, n_tok))
+    path = (n_tok <= kStreamOnly || small_batch_chunks_faster(ggml_type, rows, cols, n_tok))
                ? GQ_PATH_WEIGHT_STREAM
                : GQ_PATH_TILED;
   if (path == GQ_PATH_TILED)

@@ -11,8 +11,9 @@
 //     v_fma_mix (relative error <= 2^-11 per weight, inside the stated
 //     1e-3 of sum |w*x|); Q4_K codes reach it as fp16 subnormals, so they
 //     need no convert;
-//   * workgroup tile 128 tokens x 256 weight rows, K steps of 64 columns;
-//     8 waves, each owning 32 weight rows x all 128 tokens (4 x 1
+//   * workgroup tile 128 tokens x 256 weight rows (128 x 128 or 64 x 128
+//     when that leaves fewer CUs idle), K steps of 64 columns; 32 weight
+//     rows x all the tile's tokens per wave (BM/32 x 1
 //     v_mfma_f32_32x32x16_f16 per 16 columns);
 //   * each wave decodes its own B fragments straight into registers (no
 //     redundancy, and no LDS writes for B: LDS stores run at about a third
@@ -47,7 +48,7 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-constexpr int BM = 128, BK = 64;
+constexpr int BK = 64;
 constexpr int ROWB = BK * 2;                 // bytes of one tile row (64 fp16)
 
 // 16-byte chunk c (0..7) of tile row t lives at t * 128 + 16 * (c ^ swz(t)).
@@ -208,11 +209,11 @@ template <int T> struct BR4 {                // Q4_0 and Q5_0
 template <> struct BR<GQ_Q4_0> : BR4<GQ_Q4_0> {};
 template <> struct BR<GQ_Q5_0> : BR4<GQ_Q5_0> {};
 
-// Activations: the thread's share of one 128 x 64 tile (NT threads).  fp16:
+// Activations: the thread's share of one BM x 64 tile (NT threads).  fp16:
 // load i, thread tid covers row (NT i + tid) / 8, chunk (NT i + tid) % 8 (8
 // lanes read one 128-byte line).  fp32: row (NT i + tid) / 16, 4 columns.
-template <bool XLO, int NT> struct AR {
-  static constexpr int N = (XLO ? 2048 : 1024) / NT;
+template <bool XLO, int NT, int BM> struct AR {
+  static constexpr int N = BM * (XLO ? 16 : 8) / NT;
   u32x4 v[N];
 };
 
@@ -224,17 +225,18 @@ template <bool XLO, int NT> struct AR {
 #define GQ_GEMM_VPM (T == GQ_Q6_K ? 3 : 5)
 #endif
 
-template <int T, bool XLO, int D>
-__global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, int rows, int cols,
-                                              int rb, const void* __restrict__ xv, int n,
-                                              float* __restrict__ y, int tn, int tm) {
-  constexpr int BN = 256, NT = 512;          // 8 waves, 32 weight rows each
+template <int T, bool XLO, int D, int BN, int BM>
+__global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blob, int rows, int cols,
+                                                 int rb, const void* __restrict__ xv, int n,
+                                                 float* __restrict__ y, int tn, int tm) {
+  constexpr int NT = 2 * BN;                 // BN / 32 waves, 32 weight rows each
+  constexpr int MI = BM / 32;                // 32-token A fragments per 16 columns
   constexpr int NA = XLO ? 2 : 1;            // activation planes: hi (and lo)
   constexpr int ATILE = BM * ROWB;
   static_assert(D % 2 == 0, "even ring depth: LDS buffer parity is static");
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * NA * ATILE];
   constexpr int ES = XLO ? 4 : 2;
-  constexpr int NL = AR<XLO, NT>::N;         // activation loads per thread per step
+  constexpr int NL = AR<XLO, NT, BM>::N;     // activation loads per thread per step
 
   // tile q of XCD x covers tiles x * per .. ; token tiles of a row tile adjacent
   const int total = tn * tm, per = (total + 7) >> 3;
@@ -272,14 +274,14 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
   // With a 4-deep ring, ring slot u always holds steps = u mod 4, so only
   // slot 0 (the first step of each super-block) loads the Q4_K header.
   constexpr bool SHARE = BR<T>::kHeader && D == 4;
-  auto load = [&](AR<XLO, NT>& a, BR<T>& b, int s, auto hdr) {
+  auto load = [&](AR<XLO, NT, BM>& a, BR<T>& b, int s, auto hdr) {
     const int sg = 2 * s + fk;
     b.template load<decltype(hdr)::value>(WR, vrow, sg, sg < nseg);
     const int col = s * BK + xc;
 #pragma unroll
     for (int i = 0; i < NL; i++) a.v[i] = bld16(XR, col < cols ? xo[i] + s * BK * ES : kOobOff, 0);
   };
-  auto stage_a = [&](const AR<XLO, NT>& a, int buf) {
+  auto stage_a = [&](const AR<XLO, NT, BM>& a, int buf) {
     uint8_t* const A0 = As + buf * NA * ATILE;
 #pragma unroll
     for (int i = 0; i < NL; i++) {
@@ -299,11 +301,11 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
     }
   };
 
-  f32x16 acc[4];
+  f32x16 acc[MI];
 #pragma unroll
-  for (int i = 0; i < 4; i++) acc[i] = f32x16{};
+  for (int i = 0; i < MI; i++) acc[i] = f32x16{};
 
-  AR<XLO, NT> ra[D];
+  AR<XLO, NT, BM> ra[D];
   BR<T> rw[D];
   u32x4 bq[2][4];                            // decoded B fragments, double-buffered
   u32x4 hcur = {0, 0, 0, 0};                 // header of the current super-block (SHARE)
@@ -340,10 +342,10 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
       // decode step i + 1 while the matrix cores run step i
       decode(rw[sl], i + 1, bq[buf ^ 1], slc);
       // A fragments of sub-step ks + 1 are read while sub-step ks multiplies
-      f16x8 af[2][NA][4];
-      auto read_a = [&](int ks, f16x8 (&f)[NA][4]) {
+      f16x8 af[2][NA][MI];
+      auto read_a = [&](int ks, f16x8 (&f)[NA][MI]) {
 #pragma unroll
-        for (int mi = 0; mi < 4; mi++)
+        for (int mi = 0; mi < MI; mi++)
 #pragma unroll
           for (int p = 0; p < NA; p++)
             f[p][mi] = *reinterpret_cast<const f16x8*>(A0 + p * ATILE + mi * 32 * ROWB + fo[ks]);
@@ -354,7 +356,7 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
         if (ks + 1 < BK / 16) read_a(ks + 1, af[(ks + 1) & 1]);
         const f16x8 bf = __builtin_bit_cast(f16x8, bq[buf][ks]);
 #pragma unroll
-        for (int mi = 0; mi < 4; mi++)
+        for (int mi = 0; mi < MI; mi++)
 #pragma unroll
           for (int p = 0; p < NA; p++)
             acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ks & 1][p][mi], bf, acc[mi], 0, 0, 0);
@@ -364,9 +366,9 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
       // Shape of this step for the scheduler: the first fragments, then each
       // MFMA followed by a share of the decode VALU and the next fragment
       // read, so the matrix cores, VALU and LDS overlap within every wave.
-      __builtin_amdgcn_sched_group_barrier(0x100, 4 * NA, 0);   // DS read
+      __builtin_amdgcn_sched_group_barrier(0x100, MI * NA, 0);  // DS read
 #pragma unroll
-      for (int k = 0; k < 16 * NA; k++) {
+      for (int k = 0; k < 4 * MI * NA; k++) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, GQ_GEMM_VPM, 0);   // VALU
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
@@ -384,7 +386,7 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
   // 4 (l / 32) + v % 4
   const int r = 32 * w + fr;
 #pragma unroll
-  for (int mi = 0; mi < 4; mi++)
+  for (int mi = 0; mi < MI; mi++)
 #pragma unroll
     for (int v = 0; v < 16; v++) {
       const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
@@ -394,23 +396,59 @@ __global__ void __launch_bounds__(512) k_gemm(const uint8_t* __restrict__ blob, 
 
 namespace {
 
-template <int T, bool XLO>
-hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
-                  hipStream_t st) {
-  constexpr int BN = 256;
+template <int T, bool XLO, int BN, int BM>
+hipError_t gemm_cfg(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
+                    hipStream_t st) {
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t es = XLO ? 4 : 2;
   if ((int64_t)BN * rb >= kOobOff || (int64_t)BM * cols * es >= kOobOff) return hipErrorInvalidValue;
   const int64_t tn = (rows + BN - 1) / BN, tm = (n + BM - 1) / BM;
   if (tn * tm >= ((int64_t)1 << 31) / 8) return hipErrorInvalidValue;
   const int64_t grid = (tn * tm + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm<T, XLO, XLO ? 2 : 4>), dim3((unsigned)grid), dim3(512), 0, st,
+  hipLaunchKernelGGL((k_gemm<T, XLO, XLO ? 2 : 4, BN, BM>), dim3((unsigned)grid), dim3(2 * BN), 0, st,
                      (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tn,
                      (int)tm);
   return hipGetLastError();
 }
 
+template <int T, bool XLO>
+hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
+                  hipStream_t st) {
+  switch (gemm_tile_config(rows, n)) {
+    case 1: return gemm_cfg<T, XLO, 128, 128>(blob, rows, cols, x, n, y, st);
+    case 2: return gemm_cfg<T, XLO, 128, 64>(blob, rows, cols, x, n, y, st);
+    default: return gemm_cfg<T, XLO, 256, 128>(blob, rows, cols, x, n, y, st);
+  }
+}
+
 }  // namespace
+
+// Every tile walks its whole K range, so a shape with few tiles leaves CUs
+// idle: 256 x 128 tiles when they cover 128 to 256 CUs once; smaller tiles
+// (more workgroups resident per CU, less reuse per decoded weight) when they
+// would cover fewer CUs or the batch fits 64 tokens (128 x 64) or when they
+// need a second round (128 x 128).  Measured (fp16 x): Q4_K 4096 x 4096 at
+// 512 tokens 59 -> 36 us (128 x 64), Q6_K 4096 x 11008 at 512 tokens 300 ->
+// 144 us, Q4_K 22016 x 4096 133 -> 122 us (128 x 128), while 11008 / 12288 /
+// 14336 x 4096 stay fastest on 256 x 128.
+int gemm_tile_config(int64_t rows, int64_t n_tok) {
+  if (n_tok <= 64) return 2;
+  const int64_t big = (rows + 255) / 256 * ((n_tok + 127) / 128);
+  if (big > 256) return 1;
+  return big >= 128 ? 0 : 2;
+}
+
+// Rounds of resident tiles x K steps x the measured time of a step at that
+// tile shape, for Q4_K, Q6_K and the 32-weight types.
+double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok) {
+  static const double step_us[3][3] = {{1.05, 1.75, 1.4}, {0.9, 1.3, 1.2}, {0.57, 0.95, 0.9}};
+  static const int64_t bn[3] = {256, 128, 128}, bm[3] = {128, 128, 64}, slots[3] = {256, 512, 768};
+  const int c = gemm_tile_config(rows, n_tok);
+  const int tc = (type == GQ_Q4_K) ? 0 : (type == GQ_Q6_K) ? 1 : 2;
+  const int64_t tiles = (rows + bn[c] - 1) / bn[c] * ((n_tok + bm[c] - 1) / bm[c]);
+  return (double)((tiles + slots[c] - 1) / slots[c]) * (double)((cols + BK - 1) / BK) *
+         step_us[c][tc];
+}
 
 hipError_t launch_gemm(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, int64_t n_tok, hipStream_t st) {

@@ -119,10 +119,11 @@ int gq_matmul(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols
  * both are multiplied: about 22 of x's 24 significant bits are kept for
  * |x| >= 2^-3, values below that lose relative precision as lo reaches fp16's
  * subnormal range (absolute error <= 2^-25), and |x| must stay below 65504.
- * fp16 activations are used as given.  Up to 64 tokens the decoded weights
- * enter the products as exact integers (scaled by d and dmin in fp32), except
- * Q6_K's sc*(q-32), rounded to fp16 when its magnitude exceeds 2048; beyond 64
- * tokens each weight enters as RNE_fp16 of its fp32 dequant (the value
+ * fp16 activations are used as given.  In the weight-stream kernel (up to 32
+ * tokens, and past that when estimated faster) the decoded weights enter the
+ * products as exact integers (scaled by d and dmin in fp32), except Q6_K's
+ * sc*(q-32), rounded to fp16 when its magnitude exceeds 2048; in the tiled
+ * GEMM each weight enters as RNE_fp16 of its fp32 dequant (the value
  * gq_dequant returns with out_type GQ_F16).  Either way the relative error of
  * a product is at most 2^-11.
  */
@@ -133,7 +134,7 @@ int gq_matmul_ex(const void *weight_blob, int ggml_type, int64_t rows, int64_t c
  * gq_matmul_ex with the kernel family chosen by the caller (for tests,
  * tuning and callers that know their shapes):
  *   GQ_PATH_AUTO           what gq_matmul_ex does: n_tok = 1 -> the batch-1
- *                          GEMV; up to 64 tokens -> the weight-stream
+ *                          GEMV; up to 32 tokens -> the weight-stream
  *                          kernel; more -> the tiled matrix-core GEMM, or
  *                          the weight-stream kernel over ceil(n_tok / 64)
  *                          near-equal chunks when a cost estimate (the

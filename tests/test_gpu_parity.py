@@ -227,6 +227,29 @@ def test_gemm_partial_wave_full_size(t, rows, cols, n):
 
 
 @pytest.mark.parametrize("t,rows,cols,n,xdt", [
+    ("q4_k", 32768, 256, 100, "f16"),    # 128 tiles of 256 x 128: the large tile shape, ragged tokens
+    ("q8_0", 8400, 512, 1030, "f32"),    # 297 large tiles -> 128 x 128 tiles, ragged rows and tokens
+    ("q6_k", 1000, 768, 77, "f16"),      # few tiles -> 128 x 64 tiles, ragged rows and tokens
+    ("q4_0", 4096, 4096, 512, "f16"),    # 64 large tiles -> 256 tiles of 128 x 64
+])
+def test_gemm_tile_shapes(t, rows, cols, n, xdt):
+    """Each tile shape of the tiled GEMM (chosen by how many CUs the tiles
+    cover) with ragged edges: sampled rows (all tokens) against the oracle,
+    and two calls bit-identical."""
+    _, blob = quantized(t, rows, cols, seed=97)
+    bd = to_dev(blob)
+    say(f"gemm tile shape {t} {rows}x{cols} n={n} x={xdt}")
+    x = synth.activations(n, cols, seed=98, dtype=xdt)
+    xd = to_dev(x)
+    y0 = gq.matmul(bd, t, rows, cols, xd, path=gq.PATH_TILED).cpu().numpy()
+    y1 = gq.matmul(bd, t, rows, cols, xd, path=gq.PATH_TILED).cpu().numpy()
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    rng = np.random.default_rng(99)
+    idx = np.unique(np.concatenate([rng.choice(rows, 64, replace=False), np.r_[0:8, rows - 136:rows]]))
+    check_matmul(y0, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n} {xdt}")
+
+
+@pytest.mark.parametrize("t,rows,cols,n,xdt", [
     ("q6_k", 4096, 14336, 128, "f16"),   # few GEMM tiles over a long K: two 64-token chunks
     ("q4_k", 4096, 4096, 65, "f16"),     # chunks of 33 and 32
     ("q4_k", 1024, 4096, 130, "f32"),    # three chunks (44, 43, 43), fp32 x
