@@ -230,10 +230,12 @@ __device__ __forceinline__ int xswz(int f) {
 // (a wave holds 64/LPR rows side by side when rows are short); each wave takes
 // R such row sets per group and walks its groups pass by pass, so the double
 // buffer holds one pass whatever the row length.
-// Decode-layer fusions (template F): F_NORM stages RMSNorm(x) instead of x
-// (one more barrier, for the sum of squares); F_GLU reads a second matrix of
-// the same shape (row set 1 from blob2, the same rows as row set 0 from
-// blob) and stores silu(row set 0) * row set 1.
+// Decode-layer fusions (template F): F_NORM normalizes x (RMSNorm): fp32 x
+// stages x * gamma and scales each row's sum by the norm at the end (no
+// extra barrier: the per-wave sums of squares ride on the staging barrier),
+// fp16 x stages RNE_fp16(x * s) * gamma after one more barrier; F_GLU walks a
+// second matrix of the same shape (after a row group's passes over blob,
+// the same passes over blob2) and stores silu(first sum) * second sum.
 // A workgroup has W waves sharing one copy of x (W = 8 for long rows, where
 // x's LDS would otherwise cap the resident waves below what registers allow).
 constexpr int F_NORM = 1, F_GLU = 2;
@@ -247,14 +249,15 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
                                               float eps = 0.f) {
   extern __shared__ float xsm[];           // x padded to whole slices, then 16-column sums
   constexpr bool NORM = (F & F_NORM) != 0, GLU = (F & F_GLU) != 0;
-  static_assert(!GLU || R == 2, "the gated form takes two row sets");
+  static_assert(!GLU || R == 1, "the gated form walks one row set through both matrices");
   constexpr int RPW = 64 / LPR;            // rows side by side in a wave
-  constexpr int ROWS = GLU ? RPW : RPW * R;   // rows per group
+  constexpr int ROWS = RPW * R;            // rows per group
   // XPT = float4 of x staged per thread: cols <= XPT * 256 * W
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int nsl = (cols + 63) >> 6;        // slices per row (the last may be half)
   const int npass = (nsl + LPR - 1) / LPR;
+  const int NP = GLU ? 2 * npass : npass;  // passes per group (GLU: gate, then up)
   const int cpad = nsl << 6;
   const int ngroups = (rows + ROWS - 1) / ROWS;
   const int stride = gridDim.x * W;
@@ -281,13 +284,14 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
   // loads pass p of group grp into w; lanes past the row's last slice repeat
   // it (their sums are dropped); the descriptor ends at the matrix's last row
   auto load_item = [&](Slice<T> (&w)[R], int grp, int p) {
-    const int sl = min(p * LPR + li, nsl - 1);
+    const bool up = GLU && p >= npass;
+    const int sl = min((up ? p - npass : p) * LPR + li, nsl - 1);
     const int vo = Slice<T>::voff(sl);
 #pragma unroll
     for (int k = 0; k < R; k++) {
-      const int rw0 = uniform(grp * ROWS + (GLU ? 0 : k * RPW));
+      const int rw0 = uniform(grp * ROWS + k * RPW);
       const int nr = max(0, min(RPW, rows - rw0));
-      const uint8_t* const b = (GLU && k == 1) ? blob2 : blob;
+      const uint8_t* const b = up ? blob2 : blob;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(b + (int64_t)rw0 * rb, (uint32_t)(nr * rb));
       w[k].load(rs, sub * rb + vo, sl & 3);
     }
@@ -301,8 +305,8 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
   Slice<T> nxt[R] = {};
   auto first_two = [&]() {
     if (g < ngroups) load_item(cur, g, 0);
-    if (g < ngroups && (npass > 1 || g + stride < ngroups)) {
-      if (npass > 1) load_item(nxt, g, 1);
+    if (g < ngroups && (NP > 1 || g + stride < ngroups)) {
+      if (NP > 1) load_item(nxt, g, 1);
       else load_item(nxt, g + stride, 0);
     }
   };
@@ -311,8 +315,17 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
   // RMSNorm ("How LLM Inference Engines Work", "RMSNorm"): s = rsqrt(mean(x^2)
   // + eps) in fp32, x' = (x * s rounded to x's type) * gamma.  Every
   // workgroup forms the sum of squares itself: per thread, then the DPP
-  // network, then the W waves in order through LDS.
+  // network, then the W waves in order through LDS.  In fp32, sum w x' =
+  // s * sum w (x gamma), so fp32 x stages x * gamma now and the rows take s
+  // at the end; fp16 x must be rounded after scaling, so it waits for s.
   float* xsum = xsm + cpad;
+  float* const part = xsum + (cpad >> 4);    // W floats after the column sums
+  auto norm_scale = [&]() {
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; i += 4) tot += (part[i] + part[i + 1]) + (part[i + 2] + part[i + 3]);
+    return 1.f / sqrtf(tot / (float)cols + eps);
+  };
   if constexpr (NORM) {
     float q = 0.f;
 #pragma unroll
@@ -322,21 +335,19 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
       q += (v.x * v.x + v.y * v.y) + (v.z * v.z + v.w * v.w);
     }
     q = group_sum_dpp<64>(q);                // the wave's total in lane 63
-    float* const part = xsum + (cpad >> 4);  // W floats after the column sums
     if (lane == 63) part[wave] = q;
-    __syncthreads();
-    float tot = 0.f;
+    if constexpr (XF16) {
+      __syncthreads();
+      const float sc = norm_scale();
 #pragma unroll
-    for (int i = 0; i < W; i += 4) tot += (part[i] + part[i + 1]) + (part[i + 2] + part[i + 3]);
-    const float sc = 1.f / sqrtf(tot / (float)cols + eps);
+      for (int i = 0; i < XPT; i++)
 #pragma unroll
-    for (int i = 0; i < XPT; i++) {
+        for (int e = 0; e < 4; e++) xr[i][e] = (float)(_Float16)(xr[i][e] * sc) * gr[i][e];
+    } else {
 #pragma unroll
-      for (int e = 0; e < 4; e++) {
-        float t = xr[i][e] * sc;
-        if constexpr (XF16) t = (float)(_Float16)t;
-        xr[i][e] = t * gr[i][e];
-      }
+      for (int i = 0; i < XPT; i++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) xr[i][e] *= gr[i][e];
     }
   }
   // x (fp32, zero-padded to whole slices) into LDS; each quad of lanes holds
@@ -355,21 +366,24 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
   }
   __syncthreads();
   if constexpr (XFIRST) first_two();
+  constexpr bool LATE = NORM && !XF16;       // rows scaled by the norm at the end
+  const float rs = LATE ? norm_scale() : 1.f;
 
   bool first = true;
   for (; g < ngroups; g += stride) {
-    float acc[R];
+    float acc[R], acc_up = 0.f;
 #pragma unroll
     for (int k = 0; k < R; k++) acc[k] = 0.f;
-    for (int p = 0; p < npass; p++) {
+    for (int p = 0; p < NP; p++) {
       // next item: this group's next pass, else the next group's first
-      const bool more = (p + 1 < npass) || (g + stride < ngroups);
+      const bool more = (p + 1 < NP) || (g + stride < ngroups);
       if (more && !first) {
-        if (p + 1 < npass) load_item(nxt, g, p + 1);
+        if (p + 1 < NP) load_item(nxt, g, p + 1);
         else load_item(nxt, g + stride, 0);
       }
       first = false;
-      const int s0 = p * LPR + li;
+      const bool up = GLU && p >= npass;     // uniform: the second matrix's passes
+      const int s0 = (up ? p - npass : p) * LPR + li;
       const int s = min(s0, nsl - 1);
       const bool live = s0 < nsl;
       const bool second = (2 * s + 1) * 32 < cols;   // the slice's second half is in the row
@@ -389,7 +403,10 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
         for (int k = 0; k < R; k++) {
           // two row sets: convert + FMA pairs kept together (see dot4u_asm)
           const float d = cur[k].template dot<(R > 1)>(h, x, xs, s & 3);
-          acc[k] += use ? d : 0.f;
+          if (GLU && up)
+            acc_up += use ? d : 0.f;
+          else
+            acc[k] += use ? d : 0.f;
         }
       }
       // unconditional: without a next item the loops end here and cur is dead
@@ -399,13 +416,15 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
     if constexpr (GLU) {
       // SwiGLU ("How LLM Inference Engines Work", "SwiGLU Feed-Forward
       // Network"): silu(gate) * up, silu(v) = v / (1 + exp(-v)), in fp32
-      const float gt = group_sum_dpp<LPR>(acc[0]), up = group_sum_dpp<LPR>(acc[1]);
+      float gt = group_sum_dpp<LPR>(acc[0]), up = group_sum_dpp<LPR>(acc_up);
+      if constexpr (LATE) { gt *= rs; up *= rs; }
       const int r = g * ROWS + sub;
       if (li == LPR - 1 && r < rows) y[r] = gt / (1.f + expf(-gt)) * up;
     } else {
 #pragma unroll
       for (int k = 0; k < R; k++) {
-        const float v = group_sum_dpp<LPR>(acc[k]);        // valid in lane LPR-1 of each group
+        float v = group_sum_dpp<LPR>(acc[k]);              // valid in lane LPR-1 of each group
+        if constexpr (LATE) v *= rs;
         const int r = g * ROWS + k * RPW + sub;
         if (li == LPR - 1 && r < rows) y[r] = v;
       }
@@ -449,7 +468,7 @@ struct Fuse {
 template <int T, bool XF16, int LPR, int R, int XPT, int F, int W = 4>
 static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, const void* x,
                               float* y, const Fuse& fu, hipStream_t st) {
-  constexpr int RR = (F & F_GLU) ? 2 : R;
+  constexpr int RR = (F & F_GLU) ? 1 : R;
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t cpad = (cols + 63) / 64 * 64;
   // x, its 16-column sums and W per-wave partial sums: <= 68 KB for cols <= 16384
@@ -458,12 +477,12 @@ static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, cons
   static size_t cap_lds = 0;               // resident workgroups for the last LDS size
   static int cap = 0;                      // (both orders use the same registers)
   if (cap_lds != lds) { cap = resident_wgs(kern, 64 * W, lds); cap_lds = lds; }
-  const int64_t rpg = (F & F_GLU) ? (64 / LPR) : (64 / LPR) * RR;   // rows per group
+  const int64_t rpg = (64 / LPR) * RR;     // rows per group
   const int64_t groups = (rows + rpg - 1) / rpg;
   const int64_t wgs = (groups + W - 1) / W;
   dim3 grid((unsigned)(wgs < cap ? wgs : cap));
   // items of the wave with the most: x goes first when that is at most 2
-  const int64_t npass = ((cols + 63) / 64 + LPR - 1) / LPR;
+  const int64_t npass = ((cols + 63) / 64 + LPR - 1) / LPR * ((F & F_GLU) ? 2 : 1);
   const int64_t most = (groups + W * (int64_t)grid.x - 1) / (W * (int64_t)grid.x) * npass;
   const uint8_t* b2 = (const uint8_t*)fu.blob2;
   if (most <= 2)
