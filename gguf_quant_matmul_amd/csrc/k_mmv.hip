@@ -294,12 +294,13 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
 
 }  // namespace
 
-// grid: tiles * passes workgroups of 64 * KS threads, P tokens per pass,
+// grid: tiles * passes workgroups of 64 * KS threads (a tile is RT 16-row
+// tiles, one B fragment each, sharing the wave's activation slab), P tokens per pass,
 // KS * P * 512 bytes of LDS (twice that for fp32 activations).  With several
 // token passes the workgroup index is remapped so that the passes of one row
 // tile run back to back on one XCD (workgroups go round-robin over the 8
 // XCDs), where the tile's weights are still in that XCD's L2.
-template <int T, bool XLO, int P, int D>
+template <int T, bool XLO, int P, int D, int RT>
 __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, int rows, int cols,
                                              int rb, const void* __restrict__ xv, int n,
                                              float* __restrict__ y, int tiles, int passes) {
@@ -316,27 +317,31 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
     pass = slot % passes;
     if (tile >= tiles) return;                // whole workgroup: uniform
   }
-  const int row0 = tile * 16, tok0 = pass * P;
+  const int row0 = tile * 16 * RT, tok0 = pass * P;
   const int r = lane & 15, g = lane >> 4;
-  const int nr = min(16, rows - row0), nt = min(P, n - tok0);
+  const int nr = min(16 * RT, rows - row0), nt = min(P, n - tok0);
   const __amdgpu_buffer_rsrc_t WR = make_rsrc(blob + (int64_t)row0 * rb, (uint32_t)(nr * rb));
   const __amdgpu_buffer_rsrc_t XR =
       make_rsrc((const uint8_t*)xv + (int64_t)tok0 * cols * ES, (uint32_t)(nt * cols * ES));
   const int nslab = (cols + 255) >> 8;
   const int nblk = cols >> 5;
-  const int wl = r * rb;                      // lane's row within the tile
+  const int wl = r * rb;                      // lane's row within its 16-row tile
   uint8_t* const xw = lds + w * XB;           // this wave's activation block
 
-  auto load = [&](XS<XLO, P>& xs, WS<T>& ws, int s) {
-    if constexpr (KQ) {
-      ws.load(WR, s < nslab ? wl + s * Geo<T>::BB : kOobOff, g);
-    } else {
-      const int b0 = s * 8;
-      const int vc = wl + b0 * Geo<T>::BB;    // codes: past-the-end blocks read finite bytes
-      int vd[8];
+  auto load = [&](XS<XLO, P>& xs, WS<T> (&ws)[RT], int s) {
 #pragma unroll
-      for (int j = 0; j < 8; j++) vd[j] = (b0 + j < nblk) ? vc : kOobOff;
-      ws.load(WR, vd, vc, g);
+    for (int rt = 0; rt < RT; rt++) {
+      const int wr = wl + 16 * rt * rb;
+      if constexpr (KQ) {
+        ws[rt].load(WR, s < nslab ? wr + s * Geo<T>::BB : kOobOff, g);
+      } else {
+        const int b0 = s * 8;
+        const int vc = wr + b0 * Geo<T>::BB;  // codes: past-the-end blocks read finite bytes
+        int vd[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) vd[j] = (b0 + j < nblk) ? vc : kOobOff;
+        ws[rt].load(WR, vd, vc, g);
+      }
     }
     // activations: whole lines; columns past the row (or past the last
     // block) and tokens past the pass read as zero
@@ -351,11 +356,13 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
 
   const int cnt = (nslab - 1 - w) / KS + 1;   // this wave's slabs (w < KS <= nslab)
   constexpr int MT = kMT<P>;
-  f32x4v acc[MT];
+  f32x4v acc[RT][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) acc[mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) acc[rt][mt] = f32x4v{0.f, 0.f, 0.f, 0.f};
   XS<XLO, P> xs[D];
-  WS<T> ws[D];
+  WS<T> ws[D][RT];
 #pragma unroll
   for (int i = 0; i < D; i++) {
     load(xs[i], ws[i], w + i * KS);           // issued in ring order (see below)
@@ -374,7 +381,9 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
       // LDS operations of one wave run in order, so the block can be
       // rewritten while the previous slab's reads are still queued.
       stage_x<XLO, P>(xw, xs[i], lane);
-      slab_mma<T, XLO, P>(xw, r, ws[i], g, acc);   // slabs past cnt read as zeros
+#pragma unroll
+      for (int rt = 0; rt < RT; rt++)         // slabs past cnt read as zeros
+        slab_mma<T, XLO, P>(xw, r, ws[i][rt], g, acc[rt]);
       __builtin_amdgcn_sched_barrier(0);
       load(xs[i], ws[i], w + (m0 + i + D) * KS);
       __builtin_amdgcn_sched_barrier(0);
@@ -383,44 +392,49 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
   } while (m0 < cnt);
 
   // D lane l of tile mt holds rows (tokens) 16 mt + 4(l/16) + v of column
-  // (weight row) l % 16
+  // (weight row) l % 16 of its 16-row tile
   if (KS == 1) {
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++)
+    for (int rt = 0; rt < RT; rt++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) {
-        const int t = 16 * mt + 4 * g + v;
-        if (t < nt && r < nr) y[(int64_t)(tok0 + t) * rows + row0 + r] = acc[mt][v];
-      }
+      for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) {
+          const int t = 16 * mt + 4 * g + v, rr = 16 * rt + r;
+          if (t < nt && rr < nr) y[(int64_t)(tok0 + t) * rows + row0 + rr] = acc[rt][mt][v];
+        }
     return;
   }
   __syncthreads();                            // every wave is done with its block
-  f32x4v* red = reinterpret_cast<f32x4v*>(lds);   // [KS][MT][64]
+  f32x4v* red = reinterpret_cast<f32x4v*>(lds);   // [KS][RT][MT][64]
 #pragma unroll
-  for (int mt = 0; mt < MT; mt++) red[(w * MT + mt) * 64 + lane] = acc[mt];
+  for (int rt = 0; rt < RT; rt++)
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) red[((w * RT + rt) * MT + mt) * 64 + lane] = acc[rt][mt];
   __syncthreads();
-  for (int o = threadIdx.x; o < 256 * MT; o += blockDim.x) {
-    const int mt = o >> 8, t = (o >> 4) & 15, rr = o & 15;
+  for (int o = threadIdx.x; o < 256 * MT * RT; o += blockDim.x) {
+    const int rt = o / (256 * MT), mt = (o >> 8) % MT, t = (o >> 4) & 15, rr = o & 15;
     const int src = 16 * (t >> 2) + rr, v = t & 3;
     float sum = 0.f;
-    for (int k = 0; k < KS; k++) sum += red[(k * MT + mt) * 64 + src][v];
-    if (16 * mt + t < nt && rr < nr) y[(int64_t)(tok0 + 16 * mt + t) * rows + row0 + rr] = sum;
+    for (int k = 0; k < KS; k++) sum += red[((k * RT + rt) * MT + mt) * 64 + src][v];
+    if (16 * mt + t < nt && 16 * rt + rr < nr)
+      y[(int64_t)(tok0 + 16 * mt + t) * rows + row0 + 16 * rt + rr] = sum;
   }
 }
 
 namespace {
 
-template <int T, bool XLO, int P, int D>
+template <int T, bool XLO, int P, int D, int RT>
 hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n,
                       float* y, int ks, hipStream_t st) {
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
   const int64_t es = XLO ? 4 : 2;
   // every resource and offset must stay below the out-of-range marker
-  if (16 * rb >= kOobOff || (int64_t)P * cols * es >= kOobOff) return hipErrorInvalidValue;
-  const int64_t tiles = (rows + 15) / 16, passes = (n + P - 1) / P;
+  if (16 * RT * rb >= kOobOff || (int64_t)P * cols * es >= kOobOff) return hipErrorInvalidValue;
+  const int64_t tiles = (rows + 16 * RT - 1) / (16 * RT), passes = (n + P - 1) / P;
   const int64_t grid = passes == 1 ? tiles : (tiles + 7) / 8 * 8 * passes;
   const size_t lds = (size_t)ks * P * 512 * (XLO ? 2 : 1);
-  hipLaunchKernelGGL((k_mmv<T, XLO, P, D>), dim3((unsigned)grid), dim3(64 * ks), lds, st,
+  hipLaunchKernelGGL((k_mmv<T, XLO, P, D, RT>), dim3((unsigned)grid), dim3(64 * ks), lds, st,
                      (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tiles,
                      (int)passes);
   return hipGetLastError();
@@ -438,12 +452,15 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #ifndef GQ_MMV_DEPTH
 #define GQ_MMV_DEPTH 2                        // ring depth with fp16 activations
 #endif
+#ifndef GQ_MMV_RT2_TILES                     // 16-row tiles from which a wave takes two
+#define GQ_MMV_RT2_TILES 2000
+#endif
 
 // KS: enough waves to cover the chip GQ_MMV_WAVES / 256 deep, at most 8 per
 // workgroup (and as many as 64 KB of LDS hold), and no more than the row has
 // slabs.
-int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave) {
-  const int64_t tiles = (rows + 15) / 16, passes = (n + p - 1) / p;
+int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt) {
+  const int64_t tiles = (rows + 16 * rt - 1) / (16 * rt), passes = (n + p - 1) / p;
   const int64_t nslab = (cols + 255) / 256;
   int ks = 1;
   while (ks < 8 && (ks * 2) * lds_per_wave <= 65536 && tiles * passes * ks * 2 <= GQ_MMV_WAVES &&
@@ -458,8 +475,16 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // ring depth: as deep as the registers allow without spilling
   constexpr int D = XLO ? (P == 8 ? 2 : 1) : (P == 32) ? GQ_MMV_DEPTH32
                    : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
-  return mmv_launch<T, XLO, P, D>(blob, rows, cols, x, n, y,
-                                  pick_ks(rows, cols, n, P, P * 512 * (XLO ? 2 : 1)), st);
+  constexpr int XB = P * 512 * (XLO ? 2 : 1);
+  // Tall K-quant matrices: two 16-row tiles per wave share each activation
+  // slab, halving the activation reads, which there outweigh the weights'
+  // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;
+  // with fewer tiles the halved wave count costs more than it saves)
+  if constexpr (T == GQ_Q4_K || T == GQ_Q6_K) {
+    if ((rows + 15) / 16 >= GQ_MMV_RT2_TILES)
+      return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2), st);
+  }
+  return mmv_launch<T, XLO, P, D, 1>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 1), st);
 }
 
 template <int T, bool XLO>

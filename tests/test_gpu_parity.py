@@ -168,6 +168,25 @@ def test_mfma_many_slabs_and_rows(t):
 
 
 @pytest.mark.parametrize("t,rows,cols,ns", [
+    ("q4_k", 32768, 256, ((5, "f16"), (24, "f16"), (8, "f32"))),
+    ("q6_k", 32005, 512, ((8, "f16"), (30, "f16"), (3, "f32"))),
+])
+def test_mmv_two_tiles_per_wave(t, rows, cols, ns):
+    """Tall K-quant matrices (over 2000 16-row tiles), where each wave takes
+    two tiles sharing its activation slab; the last tile ragged: sampled rows
+    (every token) against the oracle."""
+    _, blob = quantized(t, rows, cols, seed=141)
+    bd = to_dev(blob)
+    rng = np.random.default_rng(142)
+    idx = np.unique(np.concatenate([rng.choice(rows, 96, replace=False), np.r_[0:40, rows - 40:rows]]))
+    for n, xdt in ns:
+        say(f"mmv two tiles {t} {rows}x{cols} n={n} x={xdt}")
+        x = synth.activations(n, cols, seed=143 + n, dtype=xdt)
+        y = gq.matmul(bd, t, rows, cols, to_dev(x), path=gq.PATH_WEIGHT_STREAM).cpu().numpy()
+        check_matmul(y, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n} {xdt}")
+
+
+@pytest.mark.parametrize("t,rows,cols,ns", [
     ("q4_k", 16400, 512, ((8, "f16"), (16, "f16"), (5, "f32"), (40, "f16"))),
     ("q6_k", 8200, 768, ((8, "f16"), (3, "f32"), (24, "f16"))),
 ])
