@@ -136,26 +136,70 @@ template <> struct WS<GQ_Q6_K> {     // slab = one super-block; 32-groups 2g, 2g
   }
 };
 
-// 32-weight types: slab = 8 blocks; chunk j = the lane's 8 weights of block j.
-// vd[j] is block j's offset, or an out-of-range offset when the block lies
-// past the row's end (then d reads as 0 and the block adds nothing).
+// 32-weight types: slab = 8 blocks of the row.  Lane group g loads blocks 2g
+// and 2g+1, each with whole dwords of its own bytes and a 2-byte tail (3 or
+// 4 loads per block, from a 2-byte-aligned start, none reaching past its
+// block), and stage_w regroups them through the wave's LDS into codes,
+// scales and Q5_0 high bits, so the matrix-op steps read whole words.
 template <int T> struct WS32 {
   static constexpr int BB = Geo<T>::BB;
-  u32x2 c[8];
-  uint32_t d[8], qh[8];
-  __device__ void load(__amdgpu_buffer_rsrc_t r, const int* vd, int vc, int g) {
+  static constexpr int NDW = (BB - 2) / 4;   // whole dwords per block: 8, 4, 5
+  static constexpr int CB = (T == GQ_Q8_0) ? 32 : 16;   // code bytes per block
+  static constexpr int WD = 16 * 8 * CB;     // LDS: codes [16 rows][8 blocks][CB]
+  static constexpr int WQ = WD + 256;        //      scales [16][8] fp16, then
+  static constexpr int WBYTES = WQ + (T == GQ_Q5_0 ? 512 : 0);   // high bits [16][8]
+  uint32_t raw[2][NDW + 1];                  // per block: dwords, then the tail
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-      d[j] = bld2(r, vd[j], j * BB);
-      if constexpr (T == GQ_Q8_0) c[j] = bld8(r, vc + 8 * g, j * BB + 2);
-      if constexpr (T == GQ_Q4_0) c[j] = bld8(r, vc + 8 * (g & 1), j * BB + 2);
-      if constexpr (T == GQ_Q5_0) {
-        c[j] = bld8(r, vc + 8 * (g & 1), j * BB + 6);
-        qh[j] = bld4(r, vc, j * BB + 2);
+    for (int b = 0; b < 2; b++) {
+      const int o = vo + b * BB;
+#pragma unroll
+      for (int k = 0; k < NDW / 4; k++) {
+        const u32x4 v = bld16(r, o, 16 * k);
+        raw[b][4 * k] = v.x; raw[b][4 * k + 1] = v.y; raw[b][4 * k + 2] = v.z; raw[b][4 * k + 3] = v.w;
       }
+      if constexpr (NDW % 4) raw[b][NDW - 1] = bld4(r, o, 4 * (NDW - 1));
+      raw[b][NDW] = bld2(r, o, 4 * NDW);
     }
   }
 };
+template <int T> constexpr int kWB = 0;      // weight staging bytes per wave in LDS
+template <> constexpr int kWB<GQ_Q4_0> = WS32<GQ_Q4_0>::WBYTES;
+template <> constexpr int kWB<GQ_Q5_0> = WS32<GQ_Q5_0>::WBYTES;
+template <> constexpr int kWB<GQ_Q8_0> = WS32<GQ_Q8_0>::WBYTES;
+
+// Bytes 2..5 of the dword pair (lo, hi).
+__device__ __forceinline__ uint32_t sh16(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_alignbit(hi, lo, 16);
+}
+
+// Lane (row r, group g) writes blocks 2g, 2g+1 of its row into the LDS
+// staging block ww; a block past the row's end gets scale 0 (its codes are
+// whatever bytes followed, finite, and add nothing).
+template <int T>
+__device__ __forceinline__ void stage_w(uint8_t* ww, const WS32<T>& ws, int r, int g, bool ok_a,
+                                        bool ok_b) {
+  using W = WS32<T>;
+  uint8_t* const c = ww + r * 8 * W::CB + 2 * g * W::CB;
+  uint32_t dd = 0;
+#pragma unroll
+  for (int b = 0; b < 2; b++) {
+    const uint32_t* D = ws.raw[b];            // bytes 0.. of the block, tail at D[NDW]
+    uint8_t* const cb = c + b * W::CB;
+    if constexpr (T == GQ_Q8_0) {            // d | 32 codes
+      *reinterpret_cast<u32x4*>(cb) = u32x4{sh16(D[0], D[1]), sh16(D[1], D[2]), sh16(D[2], D[3]), sh16(D[3], D[4])};
+      *reinterpret_cast<u32x4*>(cb + 16) = u32x4{sh16(D[4], D[5]), sh16(D[5], D[6]), sh16(D[6], D[7]), sh16(D[7], D[8])};
+    } else if constexpr (T == GQ_Q4_0) {     // d | 16 code bytes
+      *reinterpret_cast<u32x4*>(cb) = u32x4{sh16(D[0], D[1]), sh16(D[1], D[2]), sh16(D[2], D[3]), sh16(D[3], D[4])};
+    } else {                                 // d | 4 high-bit bytes | 16 code bytes
+      *reinterpret_cast<u32x4*>(cb) = u32x4{sh16(D[1], D[2]), sh16(D[2], D[3]), sh16(D[3], D[4]), sh16(D[4], D[5])};
+      *reinterpret_cast<uint32_t*>(ww + W::WQ + r * 32 + 8 * g + 4 * b) = sh16(D[0], D[1]);
+    }
+    if (b ? ok_b : ok_a) dd |= (D[0] & 0xFFFFu) << (16 * b);
+  }
+  *reinterpret_cast<uint32_t*>(ww + W::WD + r * 16 + 4 * g) = dd;
+}
+
 template <> struct WS<GQ_Q4_0> : WS32<GQ_Q4_0> {};
 template <> struct WS<GQ_Q5_0> : WS32<GQ_Q5_0> {};
 template <> struct WS<GQ_Q8_0> : WS32<GQ_Q8_0> {};
@@ -187,8 +231,8 @@ __device__ __forceinline__ void mma(const uint8_t* xw, int t, int k, f16x8 B, f3
 // Activation chunk of MFMA step j for lane group g: K-quant lanes own columns
 // 64 g .. 64 g + 63 (their two sub-blocks), 32-weight types 32 j + 8 g.
 template <int T, bool XLO, int P>
-__device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& ws, int g,
-                                         f32x4v (&acc)[kMT<P>]) {
+__device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, int t, const WS<T>& ws,
+                                         int g, f32x4v (&acc)[kMT<P>]) {
   constexpr int MT = kMT<P>;
   const f32x4v z = {0.f, 0.f, 0.f, 0.f};
   if constexpr (T == GQ_Q4_K) {
@@ -260,11 +304,21 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) acc[mt] += d * Pk[mt];
   } else {
+    using W = WS32<T>;
     const f16x2 off = (T == GQ_Q8_0) ? hpair(-1152.f, -1152.f)
                       : (T == GQ_Q5_0) ? hpair(-1040.f, -1040.f) : hpair(-1032.f, -1032.f);
+    // t is the lane's row in the tile (A fragments use it as the token row)
+    const u32x4 dq = *reinterpret_cast<const u32x4*>(ww + W::WD + t * 16);   // 8 fp16 scales
+    u32x4 qh4[2] = {};
+    if constexpr (T == GQ_Q5_0) {
+      qh4[0] = *reinterpret_cast<const u32x4*>(ww + W::WQ + t * 32);
+      qh4[1] = *reinterpret_cast<const u32x4*>(ww + W::WQ + t * 32 + 16);
+    }
+    const int co = t * 8 * W::CB + ((T == GQ_Q8_0) ? 8 * g : 8 * (g & 1));
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      uint32_t c0 = ws.c[j][0], c1 = ws.c[j][1];
+      const u32x2 cc = *reinterpret_cast<const u32x2*>(ww + co + j * W::CB);
+      uint32_t c0 = cc.x, c1 = cc.y;
       if constexpr (T == GQ_Q8_0) {
         c0 ^= 0x80808080u;                    // signed byte + 128
         c1 ^= 0x80808080u;
@@ -273,7 +327,7 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
         c0 = (c0 >> sh) & 0x0F0F0F0Fu;
         c1 = (c1 >> sh) & 0x0F0F0F0Fu;
         if constexpr (T == GQ_Q5_0) {
-          const uint32_t hb = ws.qh[j] >> (8 * g);   // fifth bits of elements 8g .. 8g+7
+          const uint32_t hb = qh4[j >> 2][j & 3] >> (8 * g);   // fifth bits of elements 8g .. 8g+7
           c0 |= bits_to_b4(hb);
           c1 |= bits_to_b4(hb >> 4);
         }
@@ -285,7 +339,7 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) Pk[mt] = z;
       mma<XLO, P>(xw, t, 4 * j + g, B, Pk);
-      const float dj = h2f(ws.d[j]);
+      const float dj = h2f(dq[j >> 1] >> (16 * (j & 1)));
 #pragma unroll
       for (int mt = 0; mt < MT; mt++) acc[mt] += dj * Pk[mt];
     }
@@ -296,7 +350,8 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, int t, const WS<T>& 
 
 // grid: tiles * passes workgroups of 64 * KS threads (a tile is RT 16-row
 // tiles, one B fragment each, sharing the wave's activation slab), P tokens per pass,
-// KS * P * 512 bytes of LDS (twice that for fp32 activations).  With several
+// KS * P * 512 bytes of LDS (twice that for fp32 activations; the 32-weight
+// types add their weight staging block per wave).  With several
 // token passes the workgroup index is remapped so that the passes of one row
 // tile run back to back on one XCD (workgroups go round-robin over the 8
 // XCDs), where the tile's weights are still in that XCD's L2.
@@ -307,7 +362,8 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   constexpr bool KQ = (T == GQ_Q4_K || T == GQ_Q6_K);
   constexpr int ES = XLO ? 4 : 2;
-  constexpr int XB = P * 512 * (XLO ? 2 : 1);   // LDS bytes per wave
+  constexpr int XB = P * 512 * (XLO ? 2 : 1);   // LDS bytes per wave: activations,
+  constexpr int WB = kWB<T>;                    // then staged weights (32-weight types)
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int KS = blockDim.x >> 6;
   int tile = blockIdx.x, pass = 0;
@@ -326,7 +382,8 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
   const int nslab = (cols + 255) >> 8;
   const int nblk = cols >> 5;
   const int wl = r * rb;                      // lane's row within its 16-row tile
-  uint8_t* const xw = lds + w * XB;           // this wave's activation block
+  uint8_t* const xw = lds + w * (XB + WB);    // this wave's activation block
+  uint8_t* const ww = xw + XB;                // and weight staging block
 
   auto load = [&](XS<XLO, P>& xs, WS<T> (&ws)[RT], int s) {
 #pragma unroll
@@ -334,13 +391,8 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
       const int wr = wl + 16 * rt * rb;
       if constexpr (KQ) {
         ws[rt].load(WR, s < nslab ? wr + s * Geo<T>::BB : kOobOff, g);
-      } else {
-        const int b0 = s * 8;
-        const int vc = wr + b0 * Geo<T>::BB;  // codes: past-the-end blocks read finite bytes
-        int vd[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) vd[j] = (b0 + j < nblk) ? vc : kOobOff;
-        ws[rt].load(WR, vd, vc, g);
+      } else {                                // blocks 8s + 2g, 8s + 2g + 1
+        ws[rt].load(WR, wr + (8 * s + 2 * g) * Geo<T>::BB);
       }
     }
     // activations: whole lines; columns past the row (or past the last
@@ -381,9 +433,13 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
       // LDS operations of one wave run in order, so the block can be
       // rewritten while the previous slab's reads are still queued.
       stage_x<XLO, P>(xw, xs[i], lane);
+      if constexpr (!KQ) {                    // RT is 1 for these types
+        const int b = 8 * (w + (m0 + i) * KS) + 2 * g;
+        stage_w<T>(ww, ws[i][0], r, g, b < nblk, b + 1 < nblk);
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; rt++)         // slabs past cnt read as zeros
-        slab_mma<T, XLO, P>(xw, r, ws[i][rt], g, acc[rt]);
+        slab_mma<T, XLO, P>(xw, ww, r, ws[i][rt], g, acc[rt]);
       __builtin_amdgcn_sched_barrier(0);
       load(xs[i], ws[i], w + (m0 + i + D) * KS);
       __builtin_amdgcn_sched_barrier(0);
@@ -433,7 +489,7 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
   if (16 * RT * rb >= kOobOff || (int64_t)P * cols * es >= kOobOff) return hipErrorInvalidValue;
   const int64_t tiles = (rows + 16 * RT - 1) / (16 * RT), passes = (n + P - 1) / P;
   const int64_t grid = passes == 1 ? tiles : (tiles + 7) / 8 * 8 * passes;
-  const size_t lds = (size_t)ks * P * 512 * (XLO ? 2 : 1);
+  const size_t lds = (size_t)ks * (P * 512 * (XLO ? 2 : 1) + kWB<T>);
   hipLaunchKernelGGL((k_mmv<T, XLO, P, D, RT>), dim3((unsigned)grid), dim3(64 * ks), lds, st,
                      (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tiles,
                      (int)passes);
@@ -457,13 +513,17 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #endif
 
 // KS: enough waves to cover the chip GQ_MMV_WAVES / 256 deep, at most 8 per
-// workgroup (and as many as 64 KB of LDS hold), and no more than the row has
+// workgroup (and as many as the LDS budget holds), and no more than the row has
 // slabs.
 int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt) {
   const int64_t tiles = (rows + 16 * rt - 1) / (16 * rt), passes = (n + p - 1) / p;
   const int64_t nslab = (cols + 255) / 256;
   int ks = 1;
-  while (ks < 8 && (ks * 2) * lds_per_wave <= 65536 && tiles * passes * ks * 2 <= GQ_MMV_WAVES &&
+  // 32-token passes over few tiles (the 32-weight types' staged weights on
+  // top of 16 KB of activations per wave) may take 96 KB, so 4 waves still
+  // split a long row (Q8_0 4096 x 11008 at 32 tokens: 39.6 -> 28.8 us)
+  const int budget = (p == 32 && tiles * passes <= 256) ? 98304 : 65536;
+  while (ks < 8 && (ks * 2) * lds_per_wave <= budget && tiles * passes * ks * 2 <= GQ_MMV_WAVES &&
          ks * 2 <= nslab)
     ks *= 2;
   return ks;
@@ -475,7 +535,7 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // ring depth: as deep as the registers allow without spilling
   constexpr int D = XLO ? (P == 8 ? 2 : 1) : (P == 32) ? GQ_MMV_DEPTH32
                    : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
-  constexpr int XB = P * 512 * (XLO ? 2 : 1);
+  constexpr int XB = P * 512 * (XLO ? 2 : 1) + kWB<T>;
   // Tall K-quant matrices: two 16-row tiles per wave share each activation
   // slab, halving the activation reads, which there outweigh the weights'
   // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;
