@@ -44,11 +44,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_EHIP; }
 // its time is ~ rounds of resident tiles x K steps x step time (its own
 // estimate, by tile shape), while the weight-stream kernel's time grows with
 // the number of 16-token passes: measured on MI355X, a pass streams
-// rows*cols weights at ~150 (Q6_K ~165, the 32-weight types ~65) TFLOP/s.  The batch goes to the
+// rows*cols weights at ~150 (Q6_K ~165, the 32-weight types ~80) TFLOP/s.  The batch goes to the
 // weight-stream kernel, in ceil(n/64) near-equal chunks of at most 64 tokens,
 // when that estimate is lower.
 bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_tok) {
-  const double rate = (type == GQ_Q4_K) ? 150e12 : (type == GQ_Q6_K) ? 165e12 : 65e12;
+  const double rate = (type == GQ_Q4_K) ? 150e12 : (type == GQ_Q6_K) ? 165e12 : 80e12;
   const double gemm_us = gq::gemm_estimate_us(type, rows, cols, n_tok);
   const double pass_us = (double)rows * (double)cols * 32.0 / rate * 1e6;
   const int64_t k = (n_tok + 63) / 64, base = n_tok / k, extra = n_tok % k;

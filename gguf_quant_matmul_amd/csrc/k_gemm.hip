@@ -439,12 +439,13 @@ int gemm_tile_config(int64_t rows, int64_t n_tok) {
 }
 
 // Rounds of resident tiles x K steps x the measured time of a step at that
-// tile shape, for Q4_K, Q6_K and the 32-weight types.
+// tile shape, for Q4_K, Q6_K, Q8_0 / Q5_0 and Q4_0.
 double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok) {
-  static const double step_us[3][3] = {{1.05, 1.75, 1.4}, {0.9, 1.3, 1.2}, {0.57, 0.95, 0.9}};
+  static const double step_us[3][4] = {
+      {1.05, 1.75, 1.4, 1.2}, {0.9, 1.3, 1.2, 1.0}, {0.57, 0.95, 0.7, 0.5}};
   static const int64_t bn[3] = {256, 128, 128}, bm[3] = {128, 128, 64}, slots[3] = {256, 512, 768};
   const int c = gemm_tile_config(rows, n_tok);
-  const int tc = (type == GQ_Q4_K) ? 0 : (type == GQ_Q6_K) ? 1 : 2;
+  const int tc = (type == GQ_Q4_K) ? 0 : (type == GQ_Q6_K) ? 1 : (type == GQ_Q4_0) ? 3 : 2;
   const int64_t tiles = (rows + bn[c] - 1) / bn[c] * ((n_tok + bm[c] - 1) / bm[c]);
   return (double)((tiles + slots[c] - 1) / slots[c]) * (double)((cols + BK - 1) / BK) *
          step_us[c][tc];
