@@ -167,6 +167,27 @@ def test_mfma_many_slabs_and_rows(t):
         check_matmul(y, blob, t, rows, cols, x, label=f"{t} {rows}x{cols} n={n} {xdt}")
 
 
+@pytest.mark.parametrize("t,rows,cols,n,xdt", [
+    ("q5_0", 4096, 4000, 24, "f16"),     # 32-token pass, 256 tiles: the larger LDS budget
+    ("q8_0", 4096, 4000, 30, "f16"),
+    ("q8_0", 2048, 4000, 40, "f16"),     # two 32-token passes over 128 tiles
+    ("q4_0", 4095, 2080, 9, "f32"),      # 65 blocks per row (2-byte-aligned rows), ragged tile
+    ("q5_0", 1000, 1056, 3, "f16"),      # 33 blocks: a slab with one block
+])
+def test_mmv_32weight_staged(t, rows, cols, n, xdt):
+    """The 32-weight types' small-batch path (blocks loaded whole and
+    regrouped through LDS), including rows with an odd block count and a last
+    slab of one block: sampled rows (every token) against the oracle."""
+    _, blob = quantized(t, rows, cols, seed=151)
+    bd = to_dev(blob)
+    rng = np.random.default_rng(152)
+    idx = np.unique(np.concatenate([rng.choice(rows, 80, replace=False), np.r_[0:24, rows - 24:rows]]))
+    say(f"mmv 32-weight staged {t} {rows}x{cols} n={n} x={xdt}")
+    x = synth.activations(n, cols, seed=153 + n, dtype=xdt)
+    y = gq.matmul(bd, t, rows, cols, to_dev(x), path=gq.PATH_WEIGHT_STREAM).cpu().numpy()
+    check_matmul(y, blob, t, rows, cols, x, rows_idx=idx, label=f"{t} {rows}x{cols} n={n} {xdt}")
+
+
 @pytest.mark.parametrize("t,rows,cols,ns", [
     ("q4_k", 32768, 256, ((5, "f16"), (24, "f16"), (8, "f32"))),
     ("q6_k", 32005, 512, ((8, "f16"), (30, "f16"), (3, "f32"))),
