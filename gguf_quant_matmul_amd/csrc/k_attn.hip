@@ -25,6 +25,9 @@ namespace gq {
 
 constexpr int ATT_MAX_REP = 16;           // query heads per KV head
 constexpr int ATT_LDS = 65536;            // LDS budget of the part kernel
+#ifndef GQ_ATT_COMBINE_UNROLL
+#define GQ_ATT_COMBINE_UNROLL 8           // chunks per thread in flight in the combine
+#endif
 // Largest chunk (positions) for NB blocks per row.
 constexpr int ATT_CHUNK_CAP(int nb) { return nb > 4 ? 128 : 256; }
 
@@ -338,17 +341,15 @@ __global__ void __launch_bounds__(256) k_attn_combine(const float* __restrict__ 
   const float* const p0 = part + (int64_t)h * (hd + 2);
   float mx = -INFINITY;
   for (int c = tid; c < n_chunks; c += 256) mx = fmaxf(mx, p0[c * stride + hd]);
-  red[tid] = mx;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));   // max is exact
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
   __syncthreads();
-  for (int k = 128; k >= 1; k >>= 1) {
-    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-    __syncthreads();
-  }
-  mx = red[0];
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   const int d = 32 * blockIdx.y + (tid & 31), sl = tid >> 5;
   float num = 0.f, den = 0.f;
-#pragma unroll 4
+#pragma unroll GQ_ATT_COMBINE_UNROLL
   for (int c = sl; c < n_chunks; c += 8) {
     const float* const p = p0 + c * stride;
     const float w = expf(p[hd] - mx);
