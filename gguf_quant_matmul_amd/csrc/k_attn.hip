@@ -28,6 +28,10 @@ constexpr int ATT_LDS = 65536;            // LDS budget of the part kernel
 #ifndef GQ_ATT_COMBINE_UNROLL
 #define GQ_ATT_COMBINE_UNROLL 8           // chunks per thread in flight in the combine
 #endif
+#ifndef GQ_ATT_WAVES
+#define GQ_ATT_WAVES 4
+#endif
+constexpr int ATT_WAVES(int nrp, int nb) { return nrp <= 8 && nb <= 4 ? GQ_ATT_WAVES : 1; }
 // Largest chunk (positions) for NB blocks per row.
 constexpr int ATT_CHUNK_CAP(int nb) { return nb > 4 ? 128 : 256; }
 
@@ -108,22 +112,26 @@ template <> struct KvBlock<GQ_Q4_0> {          // fp16 d, 16 bytes: low nibbles 
   }
 };
 
-// LDS layout of the part kernel, in floats except the last (byte) region:
-//   qs     [n_rep][hd]    query rows of the KV head's query heads
+// LDS layout of the part kernel, offsets in floats:
+//   qs     [n_rep][hd]    query rows of the KV head's query heads, read into
+//                         registers before the scores overwrite them
 //   sc     [nrp][chunk]   scores, then exp(s - m); rows n_rep..nrp-1 zero
+//                         (same region as qs)
 //   st     [16][2]        each head's chunk max and sum
-//   vscale [nb][chunk]    V block scales as fp32 (0 past the chunk's end)
+//   vscale [nb][chunk]    V block scales, fp16 bit patterns
 //   vcode  [chunk][cb]    V codes, cb = nb * (32 or 16) bytes per position
+// For q8_0 rows of 128 values and 5 query heads per KV head a 256-position
+// chunk takes 40,064 bytes: four workgroups share a CU's 160 KiB.
 struct AttnLds {
   int qs, sc, st, vscale, vcode, bytes;
 };
 __host__ __device__ inline AttnLds attn_lds(int n_rep, int nrp, int chunk, int nb, int cb) {
   AttnLds l;
   l.qs = 0;
-  l.sc = l.qs + n_rep * 32 * nb;
-  l.st = l.sc + nrp * chunk;
+  l.sc = 0;
+  l.st = (n_rep * 32 * nb > nrp * chunk) ? n_rep * 32 * nb : nrp * chunk;
   l.vscale = l.st + 2 * ATT_MAX_REP;
-  l.vcode = l.vscale + nb * chunk;
+  l.vcode = l.vscale + nb * chunk / 2;
   l.bytes = l.vcode * 4 + chunk * cb;
   return l;
 }
@@ -134,7 +142,8 @@ __host__ __device__ inline int attn_nrp(int n_rep) {
 }
 
 template <int KT, int NB, int NRP>
-__global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ kc,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ATT_WAVES(NRP, NB))))
+k_attn_part(const uint8_t* __restrict__ kc,
                                                    const uint8_t* __restrict__ vc,
                                                    uint32_t cache_bytes, int kv_len, int n_kv,
                                                    int n_rep, const float* __restrict__ q,
@@ -148,7 +157,7 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
   float* const qs = smem + L.qs;
   float* const sc = smem + L.sc;
   float* const st = smem + L.st;
-  float* const vscale = smem + L.vscale;
+  uint16_t* const vscale = reinterpret_cast<uint16_t*>(smem + L.vscale);
   uint8_t* const vcode = reinterpret_cast<uint8_t*>(smem + L.vcode);
   const int c = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -193,7 +202,7 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
     const int qb = tid + 256 * it, lp = qb / NB, bb = qb % NB;
     if (lp < chunk) {
       KB::store_codes(vr[it], vcode + lp * CB + bb * CBB);
-      vscale[bb * chunk + lp] = h2f(vr[it].d);
+      vscale[bb * chunk + lp] = (uint16_t)vr[it].d;
     }
   }
   __syncthreads();
@@ -217,6 +226,7 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
       ql[bb][i] = (_Float16)(v - (float)hi);
     }
   }
+  __syncthreads();                               // qs is read; sc overwrites it
 #pragma unroll
   for (int s = 0; s < TILES; s++) {
     const int tile = wave + 4 * s;
@@ -282,7 +292,8 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
   const int ng = (cnt + 3) / 4;
   for (int g4 = sl; g4 < ng; g4 += TP) {
     const int lp0 = 4 * g4;
-    const f32x4 sv = *reinterpret_cast<const f32x4*>(vscale + blk * chunk + lp0);
+    const u32x2 hv = *reinterpret_cast<const u32x2*>(vscale + blk * chunk + lp0);
+    const f32x4 sv = {h2f(hv.x), h2f(hv.x >> 16), h2f(hv.y), h2f(hv.y >> 16)};
     float v[4][4];
 #pragma unroll
     for (int k = 0; k < 4; k++) {
@@ -327,8 +338,8 @@ __global__ void __launch_bounds__(256) k_attn_part(const uint8_t* __restrict__ k
 }
 
 // out[h][d] from the per-chunk statistics, in a fixed order.  Workgroup
-// (h, column slice of 32): the largest chunk max M (a tree over
-// thread-strided maxima), then, for its 32 columns, the sums over chunks of
+// (h, column slice of 32): the largest chunk max M (thread-strided maxima,
+// then a cross-lane and a cross-wave max), then, for its 32 columns, the sums over chunks of
 // e^(m_c - M) acc_c and e^(m_c - M) l_c, each of the 8 threads of a column
 // taking every 8th chunk (their loads independent of one another), the 8
 // partial sums added in slice order.
