@@ -20,6 +20,7 @@ typedef uint16_t u16u __attribute__((aligned(1)));
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -56,6 +57,9 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int voff, int i
 }
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff + imm, 0, 0));
+}
+__device__ __forceinline__ u32x3 bld12(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
+  return __builtin_bit_cast(u32x3, __builtin_amdgcn_raw_buffer_load_b96(r, voff + imm, 0, 0));
 }
 __device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, int voff, int imm) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff + imm, 0, 0);

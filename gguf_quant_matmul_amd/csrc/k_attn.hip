@@ -58,10 +58,13 @@ template <> struct KvBlock<GQ_Q8_0> {          // fp16 d, 32 int8 codes
   __device__ static Raw load(__amdgpu_buffer_rsrc_t r, int o) {
     return Raw{bld16(r, o, 2), bld16(r, o, 18), bld2(r, o, 0)};
   }
-  // A lane's matrix-core share of a staged block: codes 8g .. 8g + 7 (at
-  // byte frag_off(g) of the block's codes) as exact fp16,
-  // (1024 + (q + 128)) - 1152.
-  __device__ static int frag_off(int g) { return 8 * g; }
+  // A lane's matrix-core share of a block: codes 8g .. 8g + 7 as exact
+  // fp16, (1024 + (q + 128)) - 1152.  They are read as a 12-byte window of
+  // the block: at byte 8g with the codes from its byte 2 (the window of
+  // g = 0 starts with d), for g = 3 at byte 22 with the codes from its byte
+  // 4, so no window reaches past the block.
+  __device__ static int win_off(int g) { return g == 3 ? 22 : 8 * g; }
+  __device__ static bool win_hi(int g) { return g == 3; }
   __device__ static f16x8 frag_codes(u32x2 c, int) {
     const f16x8 v = bytes_1024(c.x ^ 0x80808080u, c.y ^ 0x80808080u);
     return v - (_Float16)1152.f;
@@ -88,9 +91,12 @@ template <> struct KvBlock<GQ_Q4_0> {          // fp16 d, 16 bytes: low nibbles 
     uint32_t d;
   };
   __device__ static Raw load(__amdgpu_buffer_rsrc_t r, int o) { return Raw{bld16(r, o, 2), bld2(r, o, 0)}; }
-  // elements 8g .. 8g + 7: low nibbles of bytes 8g.. for g < 2, high
-  // nibbles of bytes 8(g - 2).. for g >= 2
-  __device__ static int frag_off(int g) { return 8 * (g & 1); }
+  // elements 8g .. 8g + 7: low nibbles of code bytes 8g.. for g < 2, high
+  // nibbles of code bytes 8(g - 2).. for g >= 2; the 12-byte window of
+  // g = 0, 2 is block bytes 0..11 (d first, codes from its byte 2), of
+  // g = 1, 3 block bytes 6..17 (codes from its byte 4)
+  __device__ static int win_off(int g) { return (g & 1) ? 6 : 0; }
+  __device__ static bool win_hi(int g) { return g & 1; }
   __device__ static f16x8 frag_codes(u32x2 c, int g) {
     const int sh = (g & 2) ? 4 : 0;
     const f16x8 v = bytes_1024((c.x >> sh) & 0x0F0F0F0Fu, (c.y >> sh) & 0x0F0F0F0Fu);
@@ -181,20 +187,18 @@ k_attn_part(const uint8_t* __restrict__ kc,
   }
   // K for the scores on the matrix cores: tiles of 16 positions, wave w
   // taking tiles w, w + 4, ...; lane l holds position l % 16 of the tile and
-  // codes 8(l / 16) .. 8(l / 16) + 7 of every block, with the block scales
+  // codes 8(l / 16) .. 8(l / 16) + 7 of every block, one 12-byte window
+  // load per block; the block scale is in the window of lane l % 16, which
+  // the other lanes of the position read across lanes
   const int mn = lane & 15, kg = lane >> 4;
-  u32x2 kc8[TILES][NB];
-  uint32_t kd[TILES][NB];
+  u32x3 kw[TILES][NB];
 #pragma unroll
   for (int s = 0; s < TILES; s++) {
     const int lp = 16 * (wave + 4 * s) + mn;
     const int row = t0 + min(lp, cnt - 1);       // lanes past the chunk repeat its last row
     const int o = (int)(((int64_t)row * n_kv + g) * RB);
 #pragma unroll
-    for (int bb = 0; bb < NB; bb++) {
-      kc8[s][bb] = bld8(rk, o + bb * BB, 2 + KB::frag_off(kg));
-      kd[s][bb] = bld2(rk, o + bb * BB, 0);
-    }
+    for (int bb = 0; bb < NB; bb++) kw[s][bb] = bld12(rk, o + bb * BB, KB::win_off(kg));
   }
   for (int i = tid; i < n_rep * HD; i += 256) qs[i] = q[g * n_rep * HD + i];
 #pragma unroll
@@ -234,11 +238,16 @@ k_attn_part(const uint8_t* __restrict__ kc,
     f32x4 sv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int bb = 0; bb < NB; bb++) {
-      const f16x8 B = KB::frag_codes(kc8[s][bb], kg);
+      const u32x3 w = kw[s][bb];
+      const bool hi = KB::win_hi(kg);
+      const uint32_t a0 = hi ? w.y : w.x, a1 = hi ? w.z : w.y, sh = hi ? 0u : 16u;
+      const u32x2 c8 = {__builtin_amdgcn_alignbit(a1, a0, sh), __builtin_amdgcn_alignbit(w.z, a1, sh)};
+      const f16x8 B = KB::frag_codes(c8, kg);
+      const uint32_t dsrc = (uint32_t)__shfl((int)w.x, mn, 64);   // d from lane mn's window
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       f32x4 D = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[bb], B, z, 0, 0, 0);
       D = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[bb], B, D, 0, 0, 0);
-      const float ds = h2f(kd[s][bb]);
+      const float ds = h2f(dsrc);
 #pragma unroll
       for (int v = 0; v < 4; v++) sv[v] = fmaf(D[v], ds, sv[v]);
     }
