@@ -71,7 +71,11 @@ SHAPES = [("q8_0", 1, 2, 4, 128, 1.0),       # one position: the value row
           ("q8_0", 1000, 2, 32, 128, 1.0),   # 16 query heads per KV head, several chunks
           ("q4_0", 129, 1, 3, 256, 1.0),     # head_dim 256
           ("q8_0", 5000, 8, 64, 128, 8.0),   # sharp softmax across many chunks
-          ("q4_0", 4097, 8, 32, 64, 4.0)]
+          ("q4_0", 4097, 8, 32, 64, 4.0),
+          ("q8_0", 700, 4, 4, 128, 1.0),     # one query head per KV head
+          ("q4_0", 2048, 8, 16, 128, 2.0),   # whole chunks only, 2 heads per KV head
+          ("q8_0", 513, 2, 32, 256, 1.0),    # head_dim 256, 16 heads per KV head
+          ("q8_0", 8192, 1, 8, 128, 1.0)]    # one KV head, 8 query heads, 128 whole chunks
 
 
 @pytest.mark.parametrize("t,kv_len,n_kv,n_heads,head_dim,qs", SHAPES)
