@@ -74,6 +74,7 @@ template <> struct KvBlock<GQ_Q8_0> {          // fp16 d, 32 int8 codes
     *reinterpret_cast<u32x4*>(p) = raw.a;
     *reinterpret_cast<u32x4*>(p + 16) = raw.b;
   }
+  static constexpr float BIAS = 0.f;          // value = code - BIAS
   // codes j0..j0+3 (j0 a multiple of 4) of a staged block as exact fp32
   __device__ static void code4(const uint8_t* p, int j0, float (&v)[4]) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p + j0);
@@ -106,15 +107,16 @@ template <> struct KvBlock<GQ_Q4_0> {          // fp16 d, 16 bytes: low nibbles 
   __device__ static void store_codes(const Raw& raw, uint8_t* p) {
     *reinterpret_cast<u32x4*>(p) = raw.a;
   }
-  // elements j0..j0+3: low nibbles of bytes j0.. for j0 < 16, else the high
-  // nibbles of bytes j0 - 16..
+  static constexpr float BIAS = 8.f;          // value = nibble - 8
+  // nibbles of elements j0..j0+3 (low nibbles of bytes j0.. for j0 < 16,
+  // else the high nibbles of bytes j0 - 16..) as exact fp32, bias not taken
   __device__ static void code4(const uint8_t* p, int j0, float (&v)[4]) {
     const uint32_t w = *reinterpret_cast<const uint32_t*>(p + (j0 & 15));
     const uint32_t n = ((j0 & 16) ? (w >> 4) : w) & 0x0F0F0F0Fu;
-    v[0] = ub0(n) - 8.f;
-    v[1] = ub1(n) - 8.f;
-    v[2] = ub2(n) - 8.f;
-    v[3] = ub3(n) - 8.f;
+    v[0] = ub0(n);
+    v[1] = ub1(n);
+    v[2] = ub2(n);
+    v[3] = ub3(n);
   }
 };
 
@@ -307,8 +309,15 @@ k_attn_part(const uint8_t* __restrict__ kc,
 #pragma unroll
     for (int k = 0; k < 4; k++) {
       KB::code4(vcode + (lp0 + k) * CB + blk * CBB, j0, v[k]);
+      // (q - BIAS) d as one rounding: -BIAS d is exact (BIAS is 0 or 8)
+      if constexpr (KB::BIAS != 0.f) {
+        const float nb = -KB::BIAS * sv[k];
 #pragma unroll
-      for (int e = 0; e < 4; e++) v[k][e] *= sv[k];
+        for (int e = 0; e < 4; e++) v[k][e] = fmaf(v[k][e], sv[k], nb);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; e++) v[k][e] *= sv[k];
+      }
     }
 #pragma unroll
     for (int r = 0; r < NRP; r++) {
