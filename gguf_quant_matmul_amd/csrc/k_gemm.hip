@@ -141,10 +141,13 @@ template <> struct BR<GQ_Q6_K> {
       const uint32_t H1 = (c <= 2) ? (qh.y << (4 - 2 * c)) : (qh.y >> 2);
       const uint32_t v0 = ((L0 >> sh) & 0x0F0F0F0Fu) | (H0 & 0x30303030u);
       const uint32_t v1 = ((L1 >> sh) & 0x0F0F0F0Fu) | (H1 & 0x30303030u);
-      out[c] = u32x4{h2pack(fmaf(ub0(v0), a, nb), fmaf(ub1(v0), a, nb)),
-                     h2pack(fmaf(ub2(v0), a, nb), fmaf(ub3(v0), a, nb)),
-                     h2pack(fmaf(ub0(v1), a, nb), fmaf(ub1(v1), a, nb)),
-                     h2pack(fmaf(ub2(v1), a, nb), fmaf(ub3(v1), a, nb))};
+      // codes enter as fp16 subnormals q * 2^-24; the mixed FMA rounds the
+      // exact a * (q - 32) to fp16 once, as the fp32 form above does
+      const float s = a * 16777216.f;
+      const uint32_t e0 = v0 & 0x00FF00FFu, o0 = (v0 >> 8) & 0x00FF00FFu;   // bytes 0, 2 / 1, 3
+      const uint32_t e1 = v1 & 0x00FF00FFu, o1 = (v1 >> 8) & 0x00FF00FFu;
+      out[c] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
+                     mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
     }
   }
 };
@@ -219,10 +222,10 @@ template <bool XLO, int NT, int BM> struct AR {
 
 }  // namespace
 
-// VALU instructions placed after each MFMA (measured best: 5, Q6_K's heavier
-// decode 3)
+// VALU instructions placed after each MFMA (measured best: 5; Q6_K 2, whose
+// decode has more loads per weight to wait for)
 #ifndef GQ_GEMM_VPM
-#define GQ_GEMM_VPM (T == GQ_Q6_K ? 3 : 5)
+#define GQ_GEMM_VPM (T == GQ_Q6_K ? 2 : 5)
 #endif
 
 template <int T, bool XLO, int D, int BN, int BM>
