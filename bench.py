@@ -476,7 +476,7 @@ def profile_launches(mats, n):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import torch
