@@ -51,7 +51,10 @@
  *  R7 Quantizer (used only to make test inputs): symmetric absmax per block
  *     for Q4_0/Q5_0/Q8_0/Q6_K sub-blocks and min/scale for Q4_K, in fp64, with
  *     stored fp16 scales rounded UP so every weight is covered; codes are
- *     rounded half away from zero.
+ *     rounded half away from zero.  A block whose cover would exceed the
+ *     largest finite fp16 stores 65504 instead (the pages store every scale as
+ *     an fp16, [HG §11.1]; an infinite scale would decode to NaN or Inf), so
+ *     its codes clamp at the ends of their range.
  */
 #include "gqo.h"
 #include <math.h>
@@ -65,7 +68,8 @@
  *   5 dot drops the last column, 6 dot reads x transposed,
  *   7 RMSNorm leaves out eps, 8 SiLU uses exp(+v),
  *   9 attention scores without the 1/sqrt(head_dim) scale,
- *   10 query head h reads KV head h % n_kv instead of h / n_rep. */
+ *   10 query head h reads KV head h % n_kv instead of h / n_rep,
+ *   11 a block scale with no finite cover is stored as Inf. */
 #ifndef GQO_PLANT
 #define GQO_PLANT 0
 #endif
@@ -434,7 +438,7 @@ static int clampi(double v, int lo, int hi) {
  * at the largest finite fp16 when no finite scale covers maxval. */
 static uint16_t cover_scale(double maxval, double levels) {
     uint16_t h = gqo_half_up(maxval / levels);
-    if (h > 0x7BFF) h = 0x7BFF;      /* no finite cover: saturate at 65504 */
+    if (h > 0x7BFF && GQO_PLANT != 11) h = 0x7BFF;   /* no finite cover: saturate at 65504 */
     /* make sure levels * d really covers maxval in fp64; bump one ulp if not */
     while (h < 0x7BFF && gqo_half_to_double(h) * levels < maxval) h++;
     return h;

@@ -238,6 +238,45 @@ def pin_roundtrip(o):
             assert np.all(err <= _roundtrip_bound(w, t) * (1 + 1e-9) + 1e-12), t
 
 
+def _f16_field(blob, off):
+    return int(blob[off]) | (int(blob[off + 1]) << 8)
+
+
+def pin_quantize_saturation(o):
+    """A block whose absmax needs a scale above the largest finite fp16
+    (65504) stores 65504 (0x7BFF), not Inf, and its extreme codes clamp at
+    the ends of their range, so its weights decode finite with the extremes
+    at the largest magnitudes the fields allow; an in-range block of the same
+    shape still meets the round trip.  Block: a ramp from -A to A with A four
+    times the largest magnitude the type can represent."""
+    top = 65504.0
+    big = {"q4_0": top * 7, "q5_0": top * 15, "q8_0": top * 127, "q6_k": top * 127 * 31,
+           "q4_k": top * 63 * 15}
+    for t in QTYPES:
+        qk, _ = o.block_info(t)
+        ramp = np.linspace(-1.0, 1.0, qk)
+        w = (ramp * 4.0 * big[t]).astype(np.float32)[None, :]
+        blob = o.quantize(w, t)
+        assert _f16_field(blob, 0) == 0x7BFF, (t, hex(_f16_field(blob, 0)))
+        w64 = o.dequant_f64(blob, t, 1, qk)[0]
+        assert np.all(np.isfinite(w64)), t
+        if t == "q4_k":
+            assert _f16_field(blob, 2) == 0x7BFF, (t, "dmin")
+            # sub-block 0 all negative: code 0 at min 63; sub-block 7 all
+            # positive: code 15 at scale 63, min 0
+            assert w64[0] == -top * 63 and w64[-1] == top * 63 * 15, (t, w64[0], w64[-1])
+        elif t == "q6_k":
+            assert int(blob[2]) == 127 and int(blob[2 + 15]) == 127, t      # scales clamp at 127
+            assert w64[0] == -big[t] and w64[-1] == big[t], t
+        else:
+            assert w64[0] == -big[t] and w64[-1] == big[t], (t, w64[0], w64[-1])
+        assert np.all(np.abs(w64) <= big[t]), t
+        wi = (ramp * 0.05).astype(np.float32)[None, :]
+        bi = o.quantize(wi, t)
+        err = np.abs(o.dequant_f64(bi, t, 1, qk) - wi.astype(np.float64))
+        assert np.all(err <= _roundtrip_bound(wi, t) * (1 + 1e-9) + 1e-12), t
+
+
 def pin_rmsnorm(o):
     """RMSNorm ("How LLM Inference Engines Work", "RMSNorm") against closed
     forms and invariants: x = (3, 4) has mean square 12.5, so eps = 3.5 gives
@@ -353,5 +392,6 @@ def pin_attention(o):
 
 
 ALL_PINS = [pin_golden, pin_sizes, pin_fraction_dot, pin_q8_integer, pin_q4k_structured,
+            pin_quantize_saturation,
             pin_pow2_and_perm, pin_f32_is_one_rounding, pin_roundtrip, pin_rmsnorm, pin_swiglu,
             pin_attention]

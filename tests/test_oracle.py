@@ -16,7 +16,8 @@ def test_pin(oracle, pin):
 PLANTS = {1: "nibble order swapped", 2: "Q4_K min sign", 3: "Q4_K scale/min swapped",
           4: "Q6_K offset", 5: "dot drops a column", 6: "dot reads x transposed",
           7: "RMSNorm drops eps", 8: "SiLU exponent sign",
-          9: "attention without 1/sqrt(head_dim)", 10: "attention head mapping h % n_kv"}
+          9: "attention without 1/sqrt(head_dim)", 10: "attention head mapping h % n_kv",
+          11: "unsaturated (Inf) block scale"}
 
 
 @pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda k: PLANTS[k])
