@@ -17,6 +17,7 @@ constexpr int64_t kMaxTokens = (int64_t)1 << 22;  // matrix-core grid.y = n_tok 
 constexpr int64_t kSmallBatch = 64;               // tokens per weight-stream launch at most
 constexpr int64_t kStreamOnly = 32;               // n_tok up to this: always the weight stream
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // dequant / quantize grid.x < 2^31
+constexpr int64_t kMaxCacheBytes = 0x7FFF0000;    // KV caches: below the kernels' out-of-range offset
 
 bool quant_type(int t) { return t >= GQ_Q4_0 && t <= GQ_Q6_K; }
 
@@ -205,7 +206,9 @@ int gq_attn_decode(const void* k_cache, const void* v_cache, int kv_type, int64_
   int rc = check_attn_shape(kv_len, n_kv_heads, n_heads, head_dim);
   if (rc) return rc;
   const int64_t rb = gq_row_bytes(kv_type, head_dim);
-  if (kv_len > (((int64_t)1 << 31) - 1) / ((int64_t)n_kv_heads * rb)) return GQ_EOVERFLOW;
+  // loads past the chunk's last position go to a byte offset no cache
+  // reaches (they read as zero), so the caches stay below that offset
+  if (kv_len > kMaxCacheBytes / ((int64_t)n_kv_heads * rb)) return GQ_EOVERFLOW;
   const int64_t need = gq::attn_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim);
   if (workspace_bytes < need) return GQ_EINVAL_SHAPE;
   if (!k_cache || !v_cache || !q || !out || !workspace) return GQ_EINVAL_PTR;

@@ -5,6 +5,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "../../include/gq.h"
 
@@ -190,6 +191,99 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
+}
+
+// ---------------------------------------------------------------------------
+// Exact power-of-two scaling for fp16 matrix-core operands.  fp16 covers
+// magnitudes 2^-24 .. 65504, fp32 2^-149 .. 2^128, so an fp32 value (or a
+// weight decoded in fp32) is brought into fp16 range by a factor 2^k chosen
+// from the largest magnitude m of the values that share it, and the fp32
+// results are multiplied by 2^-k; both multiplications are exact.
+
+// Exponent e with m in [2^(e-1), 2^e) (v_frexp_exp_i32_f32); m finite, > 0.
+__device__ __forceinline__ int fexp(float m) { return __builtin_amdgcn_frexp_expf(m); }
+
+// Scale exponent that puts m in [2^(top-1), 2^top); 0 when m is zero, NaN or
+// infinite (those then reach the results unchanged); clamped to +-126 so
+// that 2^k is a normal fp32 value.
+template <int TOP>
+__device__ __forceinline__ int pow2_exp_for(float m) {
+  if (!(m > 0.f) || !(m < __builtin_huge_valf())) return 0;
+  const int k = TOP - fexp(m);
+  return k > 126 ? 126 : (k < -126 ? -126 : k);
+}
+
+// {RNE_fp16(x0 s), RNE_fp16(x1 s)} and {RNE_fp16(x0 s - hi0), RNE_fp16(x1 s -
+// hi1)}: each mixed FMA forms the exact product (s a power of two) and rounds
+// once, so hi + lo keeps ~22 bits of x s; four instructions per pair.
+__device__ __forceinline__ void split2_scaled(float x0, float x1, float s, uint32_t& hi,
+                                              uint32_t& lo) {
+  asm("v_fma_mixlo_f16 %0, %1, %2, 0\n\tv_fma_mixhi_f16 %0, %3, %2, 0"
+      : "=&v"(hi) : "v"(x0), "v"(s), "v"(x1));
+  asm("v_fma_mixlo_f16 %0, %1, %2, -%4 op_sel_hi:[0,0,1]\n\t"
+      "v_fma_mixhi_f16 %0, %3, %2, -%4 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+      : "=&v"(lo) : "v"(x0), "v"(s), "v"(x1), "v"(hi));
+}
+
+// v_permlane32_swap: lanes 32..63 of a trade places with lanes 0..31 of b
+// (a = {a_lo, b_lo}, b = {a_hi, b_hi}); v_permlane16_swap: rows 1 and 3 of
+// a with rows 0 and 2 of b (rows of 16 lanes).  Written as asm because the
+// compiler's builtins for these return the first register for both results;
+// the s_nop give the wait states around a VALU write and a permlane read.
+__device__ __forceinline__ void swap32(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap16(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// max over lanes l and l ^ 32, in every lane.
+__device__ __forceinline__ float max_xor32(float v) {
+  float a = v, b = v;
+  swap32(a, b);                              // a = {v_lo, v_lo}, b = {v_hi, v_hi}
+  return fmaxf(a, b);
+}
+
+// max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane rows), in every lane.
+__device__ __forceinline__ float max_rows4(float v) {
+  float a = v, b = v;
+  swap16(a, b);                              // rows {0,0,2,2} and {1,1,3,3}
+  return max_xor32(fmaxf(a, b));
+}
+
+// Max over each 16-lane row, the result in every lane of the row.
+__device__ __forceinline__ float row16_max(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 decltype(ctrl)::value, 0xF, 0xF,
+                                                                 false));
+  };
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x128>{}));   // row_ror:8
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x124>{}));   // row_ror:4
+  v = fmaxf(v, dpp(v, std::integral_constant<int, 0x4E>{}));    // quad_perm [2,3,0,1]
+  return fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{})); // quad_perm [1,0,3,2]
+}
+
+// Per-column max over all 64 lanes of N columns m[0..N-1] (N = 8 or 16,
+// values >= 0), transposed so that few instructions serve all columns:
+// v_permlane32_swap halves the lane count per column while pairing column t
+// with t + N/2, v_permlane16_swap (rows 1 and 3 of its first operand with
+// rows 0 and 2 of its second) pairs t with t + N/4, and a row reduction
+// finishes.  Afterwards register t (t < N/4) holds in every lane of row rho
+// the max of column t + (N/4) rho.
+template <int N>
+__device__ __forceinline__ void transposed_max(float (&m)[N]) {
+  static_assert(N == 8 || N == 16, "8 or 16 columns");
+#pragma unroll
+  for (int t = 0; t < N / 2; t++) {          // lanes 0..31: column t, 32..63: t + N/2
+    swap32(m[t], m[t + N / 2]);
+    m[t] = fmaxf(m[t], m[t + N / 2]);
+  }
+#pragma unroll
+  for (int t = 0; t < N / 4; t++) {          // rows: t, t + N/4, t + N/2, t + 3N/4
+    swap16(m[t], m[t + N / 4]);
+    m[t] = row16_max(fmaxf(m[t], m[t + N / 4]));
+  }
 }
 
 }  // namespace gq

@@ -126,19 +126,21 @@ template <> struct KvBlock<GQ_Q4_0> {          // fp16 d, 16 bytes: low nibbles 
 //   sc     [nrp][chunk]   scores, then exp(s - m); rows n_rep..nrp-1 zero
 //                         (same region as qs)
 //   st     [16][2]        each head's chunk max and sum
+//   qinv   [16]           2^-k of each query head's scale (q enters as q 2^k)
 //   vscale [nb][chunk]    V block scales, fp16 bit patterns
 //   vcode  [chunk][cb]    V codes, cb = nb * (32 or 16) bytes per position
 // For q8_0 rows of 128 values and 5 query heads per KV head a 256-position
 // chunk takes 40,064 bytes: four workgroups share a CU's 160 KiB.
 struct AttnLds {
-  int qs, sc, st, vscale, vcode, bytes;
+  int qs, sc, st, qinv, vscale, vcode, bytes;
 };
 __host__ __device__ inline AttnLds attn_lds(int n_rep, int nrp, int chunk, int nb, int cb) {
   AttnLds l;
   l.qs = 0;
   l.sc = 0;
   l.st = (n_rep * 32 * nb > nrp * chunk) ? n_rep * 32 * nb : nrp * chunk;
-  l.vscale = l.st + 2 * ATT_MAX_REP;
+  l.qinv = l.st + 2 * ATT_MAX_REP;
+  l.vscale = l.qinv + ATT_MAX_REP;
   l.vcode = l.vscale + nb * chunk / 2;
   l.bytes = l.vcode * 4 + chunk * cb;
   return l;
@@ -165,6 +167,7 @@ k_attn_part(const uint8_t* __restrict__ kc,
   float* const qs = smem + L.qs;
   float* const sc = smem + L.sc;
   float* const st = smem + L.st;
+  float* const qinv = smem + L.qinv;
   uint16_t* const vscale = reinterpret_cast<uint16_t*>(smem + L.vscale);
   uint8_t* const vcode = reinterpret_cast<uint8_t*>(smem + L.vcode);
   const int c = blockIdx.x, g = blockIdx.y;
@@ -215,24 +218,38 @@ k_attn_part(const uint8_t* __restrict__ kc,
 
   // scores s = (q . K^) / sqrt(head_dim) as 16 heads x 16 positions tiles of
   // v_mfma_f32_16x16x32_f16, one 32-element block per step: A = the query
-  // rows' block as two fp16 parts (hi + lo, ~22 bits of each fp32 q), B =
-  // the block's codes (exact in fp16); each step's product is scaled by the
-  // block scale of its position (exact in fp32 up to one rounding) and
-  // summed in fp32.  Lane l of a result holds heads 4(l/16) .. +3 of
-  // position l % 16.
-  f16x8 qh[NB], ql[NB];
+  // rows' block as two fp16 parts (hi + lo, ~22 bits of each fp32 q 2^k,
+  // with 2^k per head putting its largest |q| in [2^13, 2^14), so every fp32
+  // magnitude fits), B = the block's codes (exact in fp16); each step's
+  // product is scaled by the block scale of its position (exact in fp32 up
+  // to one rounding) and summed in fp32, and the score takes 2^-k.  Lane l
+  // of a result holds heads 4(l/16) .. +3 of position l % 16.
+  float qv[NB][8];
+  float qm = 0.f;
 #pragma unroll
   for (int bb = 0; bb < NB; bb++) {
     const float* const qr = qs + mn * HD + 32 * bb + 8 * kg;
 #pragma unroll
     for (int i = 0; i < 8; i++) {
-      const float v = (mn < n_rep) ? qr[i] : 0.f;
-      const _Float16 hi = (_Float16)v;
-      qh[bb][i] = hi;
-      ql[bb][i] = (_Float16)(v - (float)hi);
+      qv[bb][i] = (mn < n_rep) ? qr[i] : 0.f;
+      qm = fmaxf(qm, fabsf(qv[bb][i]));
     }
   }
+  qm = max_rows4(qm);                            // the head's max over its 4 lane rows
+  const int qk = pow2_exp_for<14>(qm);
+  const float qsc = __builtin_ldexpf(1.f, qk);
+  if (kg == 0) qinv[mn] = __builtin_ldexpf(1.f, -qk);
+  f16x8 qh[NB], ql[NB];
+#pragma unroll
+  for (int bb = 0; bb < NB; bb++) {
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) split2_scaled(qv[bb][2 * i], qv[bb][2 * i + 1], qsc, h[i], l[i]);
+    qh[bb] = __builtin_bit_cast(f16x8, u32x4{h[0], h[1], h[2], h[3]});
+    ql[bb] = __builtin_bit_cast(f16x8, u32x4{l[0], l[1], l[2], l[3]});
+  }
   __syncthreads();                               // qs is read; sc overwrites it
+  const f32x4 qiv = *reinterpret_cast<const f32x4*>(qinv + 4 * kg);
 #pragma unroll
   for (int s = 0; s < TILES; s++) {
     const int tile = wave + 4 * s;
@@ -257,7 +274,7 @@ k_attn_part(const uint8_t* __restrict__ kc,
 #pragma unroll
     for (int v = 0; v < 4; v++) {
       const int r = 4 * kg + v;
-      if (r < n_rep && lp < chunk) sc[r * chunk + lp] = (lp < cnt) ? sv[v] * scale : -INFINITY;
+      if (r < n_rep && lp < chunk) sc[r * chunk + lp] = (lp < cnt) ? (sv[v] * qiv[v]) * scale : -INFINITY;
     }
   }
   __syncthreads();

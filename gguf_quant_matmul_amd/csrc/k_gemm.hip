@@ -5,12 +5,14 @@
 // tile ("Local LLM inference", "The mmap backend": decode once per batch,
 // reuse across its rows):
 //
-//   * B = RNE_fp16 of the stated fp32 dequant (Hitchhiker's Guide §11.2,
-//     w = (d*sc)*q - dmin*m), i.e. exactly the fp16 output of gq_dequant:
-//     every weight is decoded with one fp32 fma and rounded to fp16 by
-//     v_fma_mix (relative error <= 2^-11 per weight, inside the stated
-//     1e-3 of sum |w*x|); Q4_K codes reach it as fp16 subnormals, so they
-//     need no convert;
+//   * B = RNE_fp16(w 2^kr) of the stated fp32 dequant w (Hitchhiker's Guide
+//     §11.2, w = (d*sc)*q - dmin*m): every weight is decoded with one fp32
+//     fma on scales pre-multiplied by the row's power of two 2^kr and
+//     rounded to fp16 by v_fma_mix (relative error <= 2^-11 per weight,
+//     inside the stated 1e-3 of sum |w*x|), and y takes 2^-kr; kr follows
+//     the largest block bound of the row seen so far (every finite fp16
+//     scale then fits), the accumulators rescaled when it falls; Q4_K codes
+//     reach the mix as fp16 subnormals, so they need no convert;
 //   * workgroup tile 128 tokens x 256 weight rows (128 x 128 or 64 x 128
 //     when that leaves fewer CUs idle), K steps of 64 columns; 32 weight
 //     rows x all the tile's tokens per wave (BM/32 x 1
@@ -24,8 +26,10 @@
 //   * the raw weight bytes and activations of the next D K-steps are in
 //     flight in a register ring (loads complete in issue order, so both
 //     streams get the same distance);
-//   * fp32 activations are split into hi = RNE_fp16(x) and lo = RNE_fp16(x -
-//     hi), and both pass through the matrix op;
+//   * fp32 activations are scaled per token by a power of two 2^kx that
+//     follows the running max of |x| (accumulators rescaled when it falls),
+//     split into hi = RNE_fp16(x 2^kx) and lo = RNE_fp16(x 2^kx - hi), and
+//     both pass through the matrix op;
 //   * tiles are mapped so that the token tiles of one weight-row tile run on
 //     one XCD (workgroups go round-robin over the 8 XCDs) and share its L2.
 #include <type_traits>
@@ -49,6 +53,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 constexpr int BK = 64;
+constexpr int KNONE = 1 << 20;               // no nonzero block / activation seen yet
 constexpr int ROWB = BK * 2;                 // bytes of one tile row (64 fp16)
 
 // 16-byte chunk c (0..7) of tile row t lives at t * 128 + 16 * (c ^ swz(t)).
@@ -96,9 +101,14 @@ template <> struct BR<GQ_Q4_K> {
     if constexpr (HDR) hd = bld16(R, vo, 0);
     q = bld16(R, vo + 16 * (sg & 7), 16);
   }
-  __device__ void decode(int sg, u32x4 out[4]) const { decode(sg, hd, out); }
-  __device__ void decode(int sg, const u32x4& hd, u32x4 out[4]) const {
-    const float d = h2f(hd.x), dmin = h2f(hd.x >> 16);
+  // largest |w| the block's fields allow: 945 |d| + 63 |dmin|
+  __device__ static float bound(const u32x4& hd) {
+    return fmaf(945.f, fabsf(h2f(hd.x)), 63.f * fabsf(h2f(hd.x >> 16)));
+  }
+  __device__ float bound() const { return bound(hd); }
+  __device__ void decode(int sg, int k, u32x4 out[4]) const { decode(sg, hd, k, out); }
+  __device__ void decode(int sg, const u32x4& hd, int k, u32x4 out[4]) const {
+    const float d = __builtin_ldexpf(h2f(hd.x), k), dmin = __builtin_ldexpf(h2f(hd.x >> 16), k);
     const uint32_t f = q4k_pair(hd.y, hd.z, hd.w, sg & 7);
     const float a = d * (float)(f & 63u), nb = -(dmin * (float)(f >> 6));
     // codes enter as fp16 subnormals q * 2^-24 (high nibbles in place: 16 q)
@@ -129,8 +139,9 @@ template <> struct BR<GQ_Q6_K> {
     sc = bld2(R, vo + 2 * G, 2);
     d = bld2(R, vo, 0);
   }
-  __device__ void decode(int, u32x4 out[4]) const {
-    const float dd = h2f(d);
+  __device__ float bound() const { return 4096.f * fabsf(h2f(d)); }   // |sc (q - 32)| <= 4096
+  __device__ void decode(int, int k, u32x4 out[4]) const {
+    const float dd = __builtin_ldexpf(h2f(d), k);
 #pragma unroll
     for (int c = 0; c < 4; c++) {            // elements 8c..8c+7; scale of half c/2
       const float a = dd * (float)(int)(int8_t)(sc >> (8 * (c >> 1)));
@@ -162,8 +173,9 @@ template <> struct BR<GQ_Q8_0> {
     c0 = bld16(R, vo, 2);
     c1 = bld16(R, vo, 18);
   }
-  __device__ void decode(int, u32x4 out[4]) const {
-    const float dd = h2f(d);
+  __device__ float bound() const { return 128.f * fabsf(h2f(d)); }
+  __device__ void decode(int, int k, u32x4 out[4]) const {
+    const float dd = __builtin_ldexpf(h2f(d), k);
 #pragma unroll
     for (int c = 0; c < 4; c++) {
       const u32x4 C = (c < 2) ? c0 : c1;
@@ -189,8 +201,9 @@ template <int T> struct BR4 {                // Q4_0 and Q5_0
       c = bld16(R, vo, 2);
     }
   }
-  __device__ void decode(int, u32x4 out[4]) const {
-    const float dd = h2f(d);
+  __device__ float bound() const { return (T == GQ_Q5_0 ? 16.f : 8.f) * fabsf(h2f(d)); }
+  __device__ void decode(int, int k, u32x4 out[4]) const {
+    const float dd = __builtin_ldexpf(h2f(d), k);
     const float nb = -(float)(T == GQ_Q5_0 ? 16 : 8) * dd;
 #pragma unroll
     for (int cc = 0; cc < 4; cc++) {         // low nibbles for elements < 16
@@ -240,6 +253,14 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
   __shared__ __attribute__((aligned(16))) uint8_t As[2 * NA * ATILE];
   constexpr int ES = XLO ? 4 : 2;
   constexpr int NL = AR<XLO, NT, BM>::N;     // activation loads per thread per step
+  constexpr int NW = NT / 64;
+  // fp32 x: per token the exponent change of each staged step (double-
+  // buffered like the tile), the current exponent, and per wave whether any
+  // token of its share changed in the step
+  __shared__ __attribute__((aligned(16))) int xk[XLO ? 3 * BM + 2 * NW : 4];
+  int* const dtok = xk;                      // [2][BM]
+  int* const ktok = xk + 2 * BM;             // [BM]
+  int* const xflag = xk + 3 * BM;            // [2][NW]
 
   // tile q of XCD x covers tiles x * per .. ; token tiles of a row tile adjacent
   const int total = tn * tm, per = (total + 7) >> 3;
@@ -284,23 +305,47 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
 #pragma unroll
     for (int i = 0; i < NL; i++) a.v[i] = bld16(XR, col < cols ? xo[i] + s * BK * ES : kOobOff, 0);
   };
+  // fp32 x: thread slot i always stages the same token, 16 threads per token
+  // and step; kx[i] is that token's exponent k (x enters as hi + lo of
+  // x 2^k).  It follows the running max of |x| over the steps so far, set so
+  // that the max sits in [2^9, 2^10) and lowered (never raised) once a step's
+  // max reaches 2^14 at the current k; the accumulators are rescaled then.
+  int kx[XLO ? NL : 1];
+#pragma unroll
+  for (int i = 0; i < (XLO ? NL : 1); i++) kx[i] = KNONE;
   auto stage_a = [&](const AR<XLO, NT, BM>& a, int buf) {
     uint8_t* const A0 = As + buf * NA * ATILE;
+    bool chg = false;
 #pragma unroll
     for (int i = 0; i < NL; i++) {
       if constexpr (XLO) {
         const f32x4 f = __builtin_bit_cast(f32x4, a.v[i]);
-        float hi[4], lo[4];
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          hi[e] = (float)(_Float16)f[e];
-          lo[e] = f[e] - hi[e];
+        const float m = row16_max(fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
+        int dl = 0;
+        if (m > 0.f && m < __builtin_huge_valf()) {
+          const int e = fexp(m), k = min(126, max(-126, 10 - e));
+          if (kx[i] == KNONE) kx[i] = k;
+          else if (e + kx[i] > 14) { dl = k - kx[i]; kx[i] = k; }
         }
-        *reinterpret_cast<u32x2*>(A0 + aw[i]) = u32x2{h2pack(hi[0], hi[1]), h2pack(hi[2], hi[3])};
-        *reinterpret_cast<u32x2*>(A0 + ATILE + aw[i]) = u32x2{h2pack(lo[0], lo[1]), h2pack(lo[2], lo[3])};
+        chg |= (dl != 0);
+        const float sc = __builtin_ldexpf(1.f, kx[i] == KNONE ? 0 : kx[i]);
+        uint32_t h0, l0, h1, l1;
+        split2_scaled(f.x, f.y, sc, h0, l0);
+        split2_scaled(f.z, f.w, sc, h1, l1);
+        *reinterpret_cast<u32x2*>(A0 + aw[i]) = u32x2{h0, h1};
+        *reinterpret_cast<u32x2*>(A0 + ATILE + aw[i]) = u32x2{l0, l1};
+        if ((tid & 15) == 0) {
+          const int t = (NT * i + tid) >> 4;
+          dtok[buf * BM + t] = dl;
+          ktok[t] = kx[i];
+        }
       } else {
         *reinterpret_cast<u32x4*>(A0 + aw[i]) = a.v[i];
       }
+    }
+    if constexpr (XLO) {
+      const bool any = __builtin_amdgcn_ballot_w64(chg) != 0;
+      if (lane == 0) xflag[buf * NW + w] = any ? 1 : 0;
     }
   };
 
@@ -313,13 +358,61 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
   u32x4 bq[2][4];                            // decoded B fragments, double-buffered
   u32x4 hcur = {0, 0, 0, 0};                 // header of the current super-block (SHARE)
   auto hflag = [](auto u) { return std::integral_constant<bool, !SHARE || decltype(u)::value == 0>{}; };
+  // Weights enter B as RNE_fp16(w 2^kr), kr per row (the lane's row, both
+  // k halves agree): set from the first block with a nonzero bound U (the
+  // largest |w| its fields allow) so that U 2^kr sits in [2^9, 2^10), and
+  // lowered when a later block's U 2^kr reaches 2^14, which rescales the
+  // accumulators by the same power of two before that step's products
+  // (dpend holds the change until then).  fp16 then carries every weight
+  // within 2^-24 of its row's largest bound to 11 bits.
+  int kr = KNONE, dpend = 0;
   auto decode = [&](BR<T>& b, int s, u32x4 out[4], auto u) {
+    float U = 0.f;                           // 0: no change
     if constexpr (SHARE) {
-      if constexpr (decltype(u)::value == 0) hcur = b.hd;
-      b.decode(2 * s + fk, hcur, out);
+      // the header, and so U, changes only on a super-block's first step
+      if constexpr (decltype(u)::value == 0) {
+        hcur = b.hd;
+        U = BR<T>::bound(hcur);
+      }
     } else {
-      b.decode(2 * s + fk, out);
+      U = b.bound();
     }
+    // 32-weight types: the row's two lanes hold different blocks
+    if constexpr (T != GQ_Q4_K && T != GQ_Q6_K) U = max_xor32(U);
+    if (U > 0.f && U < __builtin_huge_valf()) {
+      const int e = fexp(U);
+      if (kr == KNONE) kr = 10 - e;         // the products so far are all zero
+      else if (e + kr > 14) { dpend += 10 - e - kr; kr = 10 - e; }
+    }
+    const int k = (kr == KNONE) ? 0 : kr;
+    if constexpr (SHARE) b.decode(2 * s + fk, hcur, k, out);
+    else b.decode(2 * s + fk, k, out);
+  };
+  // Before step i's products: bring the accumulators to step i's exponents
+  // (row: decided when step i was decoded; fp32 x: when it was staged).
+  // Both only ever fall, so this is a rare, uniform branch.
+  auto rescale = [&](int buf) {
+    bool any = __builtin_amdgcn_ballot_w64(dpend != 0) != 0;
+    if constexpr (XLO) {
+      int fl = 0;
+#pragma unroll
+      for (int j = 0; j < NW; j++) fl |= xflag[buf * NW + j];
+      any = any || __builtin_amdgcn_readfirstlane(fl) != 0;
+    }
+    if (any) {
+#pragma unroll
+      for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int qg = 0; qg < 4; qg++) {
+          int4 dt = {0, 0, 0, 0};
+          if constexpr (XLO) dt = *reinterpret_cast<const int4*>(dtok + buf * BM + 32 * mi + 8 * qg + 4 * fk);
+          acc[mi][4 * qg + 0] = __builtin_ldexpf(acc[mi][4 * qg + 0], dpend + dt.x);
+          acc[mi][4 * qg + 1] = __builtin_ldexpf(acc[mi][4 * qg + 1], dpend + dt.y);
+          acc[mi][4 * qg + 2] = __builtin_ldexpf(acc[mi][4 * qg + 2], dpend + dt.z);
+          acc[mi][4 * qg + 3] = __builtin_ldexpf(acc[mi][4 * qg + 3], dpend + dt.w);
+        }
+    }
+    dpend = 0;
   };
   static_for<D>([&](auto u) {
     load(ra[u], rw[u], u, hflag(u));         // issued in ring order
@@ -342,6 +435,8 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
       const uint8_t* const A0 = As + buf * NA * ATILE;
       constexpr int sl = (u + 1) % D;        // ring slot of step i + 1
       const std::integral_constant<int, sl> slc{};
+      rescale(buf);
+      __builtin_amdgcn_sched_barrier(0);
       // decode step i + 1 while the matrix cores run step i
       decode(rw[sl], i + 1, bq[buf ^ 1], slc);
       // A fragments of sub-step ks + 1 are read while sub-step ks multiplies
@@ -386,14 +481,18 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
   }
 
   // D lane l, register v: weight row 32 w + l % 32, token 32 mi + 8 (v / 4) +
-  // 4 (l / 32) + v % 4
+  // 4 (l / 32) + v % 4.  Steps past the last column read zeros and change
+  // no exponent, so the accumulators are at (kr, ktok) here; y takes 2^-k.
   const int r = 32 * w + fr;
+  const int kw = (kr == KNONE) ? 0 : kr;
 #pragma unroll
   for (int mi = 0; mi < MI; mi++)
 #pragma unroll
     for (int v = 0; v < 16; v++) {
       const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
-      if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = acc[mi][v];
+      int k = kw;
+      if constexpr (XLO) k += (ktok[t] == KNONE) ? 0 : ktok[t];
+      if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = __builtin_ldexpf(acc[mi][v], -k);
     }
 }
 

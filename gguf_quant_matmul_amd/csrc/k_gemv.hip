@@ -12,12 +12,11 @@
 //     runs per load, and reads past the descriptor's range return zero;
 //   * x is staged once per workgroup in LDS as fp32 (16-byte chunks XOR-
 //     swizzled per slice) with the sums of x over every 16 columns;
-//   * Q4_K and Q6_K use factored sub-block sums a*sum(q*x) - b*sum(x)
-//     (Hitchhiker's Guide §11.2, w = (d*sc)*q - dmin*m; for Q6_K the offset
-//     32 plays the min), Q4_K codes entering their products as fp16
-//     subnormals (one mixed-precision FMA per weight, no convert); the
-//     32-weight types convert each code to the signed q - offset so every
-//     product is exact relative to w; fp32 accumulation;
+//   * Q4_K uses factored sub-block sums a*sum(q*x) - b*sum(x) (Hitchhiker's
+//     Guide §11.2, w = (d*sc)*q - dmin*m), its codes entering their products
+//     as fp16 subnormals (one mixed-precision FMA per weight, no convert);
+//     Q6_K and the 32-weight types convert each code to the signed q - offset
+//     so every product is exact relative to w; fp32 accumulation;
 //   * persistent workgroups (as many as fit on the chip) loop over groups of
 //     rows with the next group's loads in flight (a wave's first two items
 //     go out before or after x is staged, by how many items it has); row
@@ -136,9 +135,11 @@ template <> struct Slice<GQ_Q6_K> {           // 32-weight groups 2j, 2j+1
     d = bld2(r, vo, 0);
   }
   template <bool ASM>
-  __device__ float dot(int g, const float* x, const float* xs, int) const {
-    // group 2j + g; unsigned codes q = low4 | high2 << 4; per 16-weight
-    // quarter sum((q - 32) * x) = sum(q * x) - 32 * sum(x)
+  __device__ float dot(int g, const float* x, const float*, int) const {
+    // group 2j + g; codes q = low4 | high2 << 4 turned into the signed bytes
+    // q - 32, so every product (q - 32) * x carries only its own rounding
+    // (summing q * x and 32 * x apart would lose the difference of two
+    // large sums); per 16-weight quarter sc * sum((q - 32) * x)
     const u32x4 L = g ? l1 : l0;
     float s0 = 0.f, s1 = 0.f;
 #pragma unroll
@@ -146,12 +147,11 @@ template <> struct Slice<GQ_Q6_K> {           // 32-weight groups 2j, 2j+1
       const uint32_t H = h[2 * g + (k & 1)];
       const uint32_t lo = (L[k] & 0x0F0F0F0Fu) | q6k_hi(H, k >> 1);
       const uint32_t hi = ((L[k] >> 4) & 0x0F0F0F0Fu) | q6k_hi(H, 2 + (k >> 1));
-      s0 = dot4u_asm(lo, x + 4 * k, s0);
-      s1 = dot4u_asm(hi, x + 16 + 4 * k, s1);
+      s0 = dot4s_asm(centre<32>(lo), x + 4 * k, s0);
+      s1 = dot4s_asm(centre<32>(hi), x + 16 + 4 * k, s1);
     }
     const uint32_t sc2 = sc >> (16 * g);
-    const float r = fmaf(sb1(sc2), fmaf(-32.f, xs[1], s1), sb0(sc2) * fmaf(-32.f, xs[0], s0));
-    return h2f(d) * r;
+    return h2f(d) * fmaf(sb1(sc2), s1, sb0(sc2) * s0);
   }
 };
 
@@ -442,16 +442,12 @@ __global__ void __launch_bounds__(64 * W) k_gemv(const uint8_t* __restrict__ blo
 #define GQ_GEMV_LONG_W 8
 #endif
 
+// Workgroups of kern that fit on device dev at once.
 template <typename K>
-static int resident_wgs(K kern, int threads, size_t lds) {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-  }
-  int per = 0;
+static int resident_wgs(K kern, int dev, int threads, size_t lds) {
+  int cus = 0, per = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, (const void*)kern, threads, lds) != hipSuccess ||
       per < 1)
     per = 1;
@@ -474,13 +470,23 @@ static hipError_t gemv_launch(const void* blob, int64_t rows, int64_t cols, cons
   // x, its 16-column sums and W per-wave partial sums: <= 68 KB for cols <= 16384
   const size_t lds = (size_t)cpad * 4 + (size_t)(cpad / 16) * 4 + 4 * W;
   auto kern = k_gemv<T, XF16, LPR, RR, XPT, false, F, W>;
-  static size_t cap_lds = 0;               // resident workgroups for the last LDS size
-  static int cap = 0;                      // (both orders use the same registers)
-  if (cap_lds != lds) { cap = resident_wgs(kern, 64 * W, lds); cap_lds = lds; }
+  // resident workgroups for the last (device, LDS size) this host thread
+  // launched with (both orders use the same registers); per thread, so
+  // concurrent callers share nothing
+  struct Occ {
+    int dev;
+    size_t lds;
+    int cap;
+  };
+  thread_local Occ occ = {-1, 0, 1};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (occ.dev != dev || occ.lds != lds) occ = Occ{dev, lds, resident_wgs(kern, dev, 64 * W, lds)};
+  const int cap = occ.cap;
   const int64_t rpg = (64 / LPR) * RR;     // rows per group
   const int64_t groups = (rows + rpg - 1) / rpg;
   const int64_t wgs = (groups + W - 1) / W;
-  dim3 grid((unsigned)(wgs < cap ? wgs : cap));
+  dim3 grid((unsigned)(wgs < cap ? wgs : cap));   // wgs >= 1, cap >= 1
   // items of the wave with the most: x goes first when that is at most 2
   const int64_t npass = ((cols + 63) / 64 + LPR - 1) / LPR * ((F & F_GLU) ? 2 : 1);
   const int64_t most = (groups + W * (int64_t)grid.x - 1) / (W * (int64_t)grid.x) * npass;

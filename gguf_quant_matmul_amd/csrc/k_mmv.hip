@@ -27,8 +27,10 @@
 //     term as a second product of x with m (<= 63), both scaled by the
 //     block's d and dmin in fp32; Q6_K B = RNE_fp16(sc*(q-32)) (exact unless
 //     |sc*(q-32)| > 2048); Q4_0 / Q5_0 / Q8_0 B = q - offset with d applied
-//     per block in fp32.  fp32 x is split into two fp16 parts (hi, lo) that
-//     both go through the matrix op;
+//     per block in fp32.  fp32 x is scaled per token and slab by a power of
+//     two from the slab's largest |x| (any fp32 magnitude then fits fp16),
+//     split into two fp16 parts (hi, lo) that both go through the matrix op,
+//     and the slab's products take the inverse power;
 //   * the KS partial tiles are summed in LDS in wave order, so the result is
 //     the same on every run.
 #include "gq_device.h"
@@ -74,33 +76,65 @@ template <bool XLO, int P> struct XS {
 // The wave's LDS block: token t's 256 columns at t * 512 bytes, 16-byte chunk
 // k stored at position k ^ (t & 7), so the 8 lanes that LDS serves together
 // hit 8 different bank groups both when storing a load's chunks and when
-// reading A fragments.  fp32 activations store hi = RNE_fp16(x) in the first
-// P rows and lo = RNE_fp16(x - hi) in the next P.
+// reading A fragments.  fp32 activations store hi = RNE_fp16(x s) in the
+// first P rows and lo = RNE_fp16(x s - hi) in the next P, where s = 2^k is
+// chosen per token and slab from the slab's largest |x| (so |x s| < 2^14:
+// every fp32 magnitude fits fp16, and hi + lo keeps ~22 bits of each value
+// within 2^-17 of that largest one); the slab's products are multiplied by
+// 2^-k when they join the accumulators.
 __device__ __forceinline__ int xslot(int t, int k) { return t * 512 + ((k ^ (t & 7)) << 4); }
 
+// Bytes of the per-wave scale block after the weight staging: s[16], 1/s[16].
+template <bool XLO> constexpr int kSB = XLO ? 128 : 0;
+
 template <bool XLO, int P>
-__device__ __forceinline__ void stage_x(uint8_t* xw, const XS<XLO, P>& xs, int lane) {
+__device__ __forceinline__ void stage_x(uint8_t* xw, float* sv, const XS<XLO, P>& xs, int lane) {
   if constexpr (!XLO) {
 #pragma unroll
     for (int i = 0; i < P / 2; i++)
       *reinterpret_cast<u32x4*>(xw + xslot(2 * i + (lane >> 5), lane & 31)) = xs.v[i];
   } else {
+    // each token's largest |x| over the slab (lane l holds its columns 4l..4l+3)
+    float m[P];
 #pragma unroll
     for (int i = 0; i < P; i++) {
       const f32x4 f = __builtin_bit_cast(f32x4, xs.v[i]);
-      f16x2 h[2], l[2];
+      m[i] = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+    }
+    transposed_max<P>(m);                   // register j, row rho: token j + (P/4) rho
+    if ((lane & 15) == 0) {
 #pragma unroll
-      for (int e = 0; e < 2; e++) {
-        const _Float16 a = (_Float16)f[2 * e], b = (_Float16)f[2 * e + 1];
-        h[e] = f16x2{a, b};
-        l[e] = f16x2{(_Float16)(f[2 * e] - (float)a), (_Float16)(f[2 * e + 1] - (float)b)};
+      for (int j = 0; j < P / 4; j++) {
+        const int k = pow2_exp_for<14>(m[j]), t = j + (P / 4) * (lane >> 4);
+        sv[t] = __builtin_ldexpf(1.f, k);
+        sv[16 + t] = __builtin_ldexpf(1.f, -k);
       }
+    }
+    float s[P];                              // every lane: the scale of every token
+#pragma unroll
+    for (int q = 0; q < P / 4; q++) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(sv + 4 * q);
+      s[4 * q] = v.x; s[4 * q + 1] = v.y; s[4 * q + 2] = v.z; s[4 * q + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < P; i++) {
+      const f32x4 f = __builtin_bit_cast(f32x4, xs.v[i]);
+      uint32_t h0, l0, h1, l1;
+      split2_scaled(f.x, f.y, s[i], h0, l0);
+      split2_scaled(f.z, f.w, s[i], h1, l1);
       const int o = xslot(i, lane >> 1) + 8 * (lane & 1);
-      *reinterpret_cast<u32x2*>(xw + o) = u32x2{__builtin_bit_cast(uint32_t, h[0]), __builtin_bit_cast(uint32_t, h[1])};
-      *reinterpret_cast<u32x2*>(xw + P * 512 + o) =
-          u32x2{__builtin_bit_cast(uint32_t, l[0]), __builtin_bit_cast(uint32_t, l[1])};
+      *reinterpret_cast<u32x2*>(xw + o) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(xw + P * 512 + o) = u32x2{l0, l1};
     }
   }
+}
+
+// 1/s of the four tokens 4g .. 4g+3 whose results lane group g accumulates
+// (with P = 8 tokens 8..15 repeat 0..7 and are not stored).
+template <bool XLO, int P>
+__device__ __forceinline__ f32x4 inv_scales(const float* sv, int g) {
+  if constexpr (!XLO) return f32x4{1.f, 1.f, 1.f, 1.f};
+  else return *reinterpret_cast<const f32x4*>(sv + 16 + ((4 * g) & (P - 1)));
 }
 
 // A fragment (8 consecutive columns, chunk k of the slab) of token row t.
@@ -231,10 +265,11 @@ __device__ __forceinline__ void mma(const uint8_t* xw, int t, int k, f16x8 B, f3
 // Activation chunk of MFMA step j for lane group g: K-quant lanes own columns
 // 64 g .. 64 g + 63 (their two sub-blocks), 32-weight types 32 j + 8 g.
 template <int T, bool XLO, int P>
-__device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, int t, const WS<T>& ws,
-                                         int g, f32x4v (&acc)[kMT<P>]) {
+__device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, const float* sv, int t,
+                                         const WS<T>& ws, int g, f32x4v (&acc)[kMT<P>]) {
   constexpr int MT = kMT<P>;
   const f32x4v z = {0.f, 0.f, 0.f, 0.f};
+  const f32x4 iv = inv_scales<XLO, P>(sv, g);   // fp32 x: undo the slab's scale
   if constexpr (T == GQ_Q4_K) {
     const float d = h2f(ws.hd.x), dmin = h2f(ws.hd.x >> 16);
     f16x8 M[2];
@@ -277,8 +312,13 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, i
     }
 #pragma unroll
     for (int mt = 0; mt < MT; mt++) {
-      acc[mt] += d * Pk[mt];
-      acc[mt] -= dmin * Pm[mt];
+      if constexpr (XLO) {
+        acc[mt] += (d * iv) * Pk[mt];
+        acc[mt] -= (dmin * iv) * Pm[mt];
+      } else {
+        acc[mt] += d * Pk[mt];
+        acc[mt] -= dmin * Pm[mt];
+      }
     }
   } else if constexpr (T == GQ_Q6_K) {
     const float d = h2f(ws.d);
@@ -302,7 +342,10 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, i
       mma<XLO, P>(xw, t, 8 * g + j, B, Pk);
     }
 #pragma unroll
-    for (int mt = 0; mt < MT; mt++) acc[mt] += d * Pk[mt];
+    for (int mt = 0; mt < MT; mt++) {
+      if constexpr (XLO) acc[mt] += (d * iv) * Pk[mt];
+      else acc[mt] += d * Pk[mt];
+    }
   } else {
     using W = WS32<T>;
     const f16x2 off = (T == GQ_Q8_0) ? hpair(-1152.f, -1152.f)
@@ -315,6 +358,9 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, i
       qh4[1] = *reinterpret_cast<const u32x4*>(ww + W::WQ + t * 32 + 16);
     }
     const int co = t * 8 * W::CB + ((T == GQ_Q8_0) ? 8 * g : 8 * (g & 1));
+    f32x4v as[MT];                            // fp32 x: the slab's sum before 1/s
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) as[mt] = z;
 #pragma unroll
     for (int j = 0; j < 8; j++) {
       const u32x2 cc = *reinterpret_cast<const u32x2*>(ww + co + j * W::CB);
@@ -341,7 +387,14 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, i
       mma<XLO, P>(xw, t, 4 * j + g, B, Pk);
       const float dj = h2f(dq[j >> 1] >> (16 * (j & 1)));
 #pragma unroll
-      for (int mt = 0; mt < MT; mt++) acc[mt] += dj * Pk[mt];
+      for (int mt = 0; mt < MT; mt++) {
+        if constexpr (XLO) as[mt] += dj * Pk[mt];
+        else acc[mt] += dj * Pk[mt];
+      }
+    }
+    if constexpr (XLO) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] += iv * as[mt];
     }
   }
 }
@@ -382,8 +435,10 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
   const int nslab = (cols + 255) >> 8;
   const int nblk = cols >> 5;
   const int wl = r * rb;                      // lane's row within its 16-row tile
-  uint8_t* const xw = lds + w * (XB + WB);    // this wave's activation block
-  uint8_t* const ww = xw + XB;                // and weight staging block
+  constexpr int SB = kSB<XLO>;                 // then fp32 x's per-token scales
+  uint8_t* const xw = lds + w * (XB + WB + SB);   // this wave's activation block,
+  uint8_t* const ww = xw + XB;                // weight staging block
+  float* const sv = reinterpret_cast<float*>(ww + WB);   // and scales
 
   auto load = [&](XS<XLO, P>& xs, WS<T> (&ws)[RT], int s) {
 #pragma unroll
@@ -432,14 +487,14 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
       // of the unrolled body, which would make every step wait on them all.
       // LDS operations of one wave run in order, so the block can be
       // rewritten while the previous slab's reads are still queued.
-      stage_x<XLO, P>(xw, xs[i], lane);
+      stage_x<XLO, P>(xw, sv, xs[i], lane);
       if constexpr (!KQ) {                    // RT is 1 for these types
         const int b = 8 * (w + (m0 + i) * KS) + 2 * g;
         stage_w<T>(ww, ws[i][0], r, g, b < nblk, b + 1 < nblk);
       }
 #pragma unroll
       for (int rt = 0; rt < RT; rt++)         // slabs past cnt read as zeros
-        slab_mma<T, XLO, P>(xw, ww, r, ws[i][rt], g, acc[rt]);
+        slab_mma<T, XLO, P>(xw, ww, sv, r, ws[i][rt], g, acc[rt]);
       __builtin_amdgcn_sched_barrier(0);
       load(xs[i], ws[i], w + (m0 + i + D) * KS);
       __builtin_amdgcn_sched_barrier(0);
@@ -489,7 +544,7 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
   if (16 * RT * rb >= kOobOff || (int64_t)P * cols * es >= kOobOff) return hipErrorInvalidValue;
   const int64_t tiles = (rows + 16 * RT - 1) / (16 * RT), passes = (n + P - 1) / P;
   const int64_t grid = passes == 1 ? tiles : (tiles + 7) / 8 * 8 * passes;
-  const size_t lds = (size_t)ks * (P * 512 * (XLO ? 2 : 1) + kWB<T>);
+  const size_t lds = (size_t)ks * (P * 512 * (XLO ? 2 : 1) + kWB<T> + kSB<XLO>);
   hipLaunchKernelGGL((k_mmv<T, XLO, P, D, RT>), dim3((unsigned)grid), dim3(64 * ks), lds, st,
                      (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tiles,
                      (int)passes);
@@ -535,7 +590,7 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // ring depth: as deep as the registers allow without spilling
   constexpr int D = XLO ? (P == 8 ? 2 : 1) : (P == 32) ? GQ_MMV_DEPTH32
                    : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
-  constexpr int XB = P * 512 * (XLO ? 2 : 1) + kWB<T>;
+  constexpr int XB = P * 512 * (XLO ? 2 : 1) + kWB<T> + kSB<XLO>;
   // Tall K-quant matrices: two 16-row tiles per wave share each activation
   // slab, halving the activation reads, which there outweigh the weights'
   // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;

@@ -115,17 +115,26 @@ int gq_matmul(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols
  * For n_tok >= 2 the weights are decoded once per call and reused for every
  * token ("Local LLM inference", "The mmap backend": decode each projection
  * weight once per input batch) on the matrix cores.  fp32 activations are then
- * split into two fp16 parts, hi = RNE_fp16(x) and lo = RNE_fp16(x - hi), and
- * both are multiplied: about 22 of x's 24 significant bits are kept for
- * |x| >= 2^-3, values below that lose relative precision as lo reaches fp16's
- * subnormal range (absolute error <= 2^-25), and |x| must stay below 65504.
- * fp16 activations are used as given.  In the weight-stream kernel (up to 32
- * tokens, and past that when estimated faster) the decoded weights enter the
- * products as exact integers (scaled by d and dmin in fp32), except Q6_K's
- * sc*(q-32), rounded to fp16 when its magnitude exceeds 2048; in the tiled
- * GEMM each weight enters as RNE_fp16 of its fp32 dequant (the value
- * gq_dequant returns with out_type GQ_F16).  Either way the relative error of
- * a product is at most 2^-11.
+ * scaled by an exact power of two 2^k per token (and per 256-column slab in
+ * the weight-stream kernel, per running maximum in the tiled GEMM) that puts
+ * the largest |x| near 2^10..2^14, split into two fp16 parts, hi =
+ * RNE_fp16(x 2^k) and lo = RNE_fp16(x 2^k - hi), both multiplied, and the
+ * fp32 results multiplied by 2^-k: any finite fp32 magnitude is accepted,
+ * about 22 of x's 24 significant bits are kept, and only values more than
+ * 2^17 below the largest |x| of their scope lose relative precision (each
+ * with an absolute error below 2^-34 of that largest |x|).  fp16 activations
+ * are used as given.  In the weight-stream kernel (up to 32 tokens, and past
+ * that when estimated faster) the decoded weights enter the products as
+ * exact integers (scaled by d and dmin in fp32), except Q6_K's sc*(q-32),
+ * rounded to fp16 when its magnitude exceeds 2048; in the tiled GEMM each
+ * weight enters as RNE_fp16(w 2^r) of its fp32 dequant w, with a power of
+ * two 2^r per weight row that follows the largest magnitude its blocks'
+ * fields allow (so every finite block scale is accepted).  Either way the
+ * relative error of a product is at most 2^-11.  Q4_K's min term is summed
+ * apart from its scale term (w = a*q - b gives a*sum(q*x) - b*sum(x) in the
+ * batch-1 GEMV and the weight-stream kernel), so on blocks where a*q and b
+ * nearly cancel the error is relative to sum(|a|*q*|x| + |b|*|x|) rather
+ * than to sum|w*x|; blocks a quantizer makes do not come near that.
  */
 int gq_matmul_ex(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
                  const void *x, int x_type, float *y, int64_t n_tok, void *stream);
@@ -219,8 +228,8 @@ int gq_quantize(const float *w, int ggml_type, int64_t rows, int64_t cols,
  *   workspace         device, at least gq_attn_decode_workspace_bytes(...)
  *                     bytes (per-chunk softmax statistics), contents ignored
  *                     and overwritten; one per concurrent call
- * All pointers 16-byte aligned; out and workspace overlap nothing else.  The
- * cache must stay below 2^31 bytes (GQ_EOVERFLOW).  The result does not
+ * All pointers 16-byte aligned; out and workspace overlap nothing else.  Each
+ * cache must stay within 0x7FFF0000 bytes (GQ_EOVERFLOW).  The result does not
  * depend on the run: positions are split into fixed chunks and combined in
  * order.
  */
