@@ -56,6 +56,8 @@ def lib():
         L.gq_attn_decode_workspace_bytes.restype = i64
         L.gq_attn_decode.argtypes = [vp, vp, ci, i64, ci, ci, vp, ci, vp, vp, i64, vp]
         L.gq_attn_decode.restype = ci
+        L.gq_attn_decode_noalloc.argtypes = [vp, vp, ci, i64, ci, ci, vp, ci, vp, vp]
+        L.gq_attn_decode_noalloc.restype = ci
         L.gq_probe_stream_read.argtypes = [vp, i64, vp, vp]
         L.gq_probe_stream_read.restype = ci
         L.gq_dequant.argtypes = [vp, ci, i64, i64, vp, ci, vp]
@@ -181,6 +183,22 @@ def attn_decode(k_cache, v_cache, t, kv_len: int, n_kv_heads: int, head_dim: int
                               workspace.data_ptr(), workspace.numel(), _stream(stream))
     if rc:
         raise GQError(rc, "gq_attn_decode")
+    return out
+
+
+def attn_decode_noalloc(k_cache, v_cache, t, kv_len: int, n_kv_heads: int, head_dim: int, q,
+                        out, stream=None):
+    """attn_decode through gq_attn_decode_noalloc: the library's fixed
+    device array serves as workspace; out (fp32 [n_heads, head_dim], CUDA)
+    is given by the caller, so the call itself allocates nothing."""
+    import torch
+    if q.dtype != torch.float32 or not q.is_contiguous():
+        raise TypeError("q must be contiguous float32")
+    rc = lib().gq_attn_decode_noalloc(k_cache.data_ptr(), v_cache.data_ptr(), _tid(t), kv_len,
+                                      n_kv_heads, head_dim, q.data_ptr(), q.shape[0],
+                                      out.data_ptr(), _stream(stream))
+    if rc:
+        raise GQError(rc, "gq_attn_decode_noalloc")
     return out
 
 

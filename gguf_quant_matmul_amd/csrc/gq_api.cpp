@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/gq.h"
 #include "gq_launch.h"
 
@@ -199,9 +202,11 @@ int64_t gq_attn_decode_workspace_bytes(int64_t kv_len, int n_kv_heads, int n_hea
   return gq::attn_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim);
 }
 
-int gq_attn_decode(const void* k_cache, const void* v_cache, int kv_type, int64_t kv_len,
-                   int n_kv_heads, int head_dim, const float* q, int n_heads, float* out,
-                   void* workspace, int64_t workspace_bytes, void* stream) {
+// Checks shared by the attention entry points: everything but the
+// workspace.  need receives the workspace bytes the call takes.
+static int check_attn(const void* k_cache, const void* v_cache, int kv_type, int64_t kv_len,
+                      int n_kv_heads, int head_dim, const float* q, int n_heads, const float* out,
+                      int64_t* need) {
   if (kv_type != GQ_Q8_0 && kv_type != GQ_Q4_0) return GQ_EINVAL_TYPE;
   int rc = check_attn_shape(kv_len, n_kv_heads, n_heads, head_dim);
   if (rc) return rc;
@@ -209,22 +214,92 @@ int gq_attn_decode(const void* k_cache, const void* v_cache, int kv_type, int64_
   // loads past the chunk's last position go to a byte offset no cache
   // reaches (they read as zero), so the caches stay below that offset
   if (kv_len > kMaxCacheBytes / ((int64_t)n_kv_heads * rb)) return GQ_EOVERFLOW;
-  const int64_t need = gq::attn_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim);
-  if (workspace_bytes < need) return GQ_EINVAL_SHAPE;
-  if (!k_cache || !v_cache || !q || !out || !workspace) return GQ_EINVAL_PTR;
-  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out) ||
-      !aligned16(workspace))
+  *need = gq::attn_workspace_bytes(kv_len, n_kv_heads, n_heads, head_dim);
+  if (!k_cache || !v_cache || !q || !out) return GQ_EINVAL_PTR;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q) || !aligned16(out))
     return GQ_EALIGN;
   const int64_t cbytes = kv_len * n_kv_heads * rb;
   const int64_t qbytes = (int64_t)n_heads * head_dim * 4;
   if (overlap(out, qbytes, q, qbytes) || overlap(out, qbytes, k_cache, cbytes) ||
-      overlap(out, qbytes, v_cache, cbytes) || overlap(out, qbytes, workspace, need) ||
-      overlap(workspace, need, q, qbytes) || overlap(workspace, need, k_cache, cbytes) ||
-      overlap(workspace, need, v_cache, cbytes))
+      overlap(out, qbytes, v_cache, cbytes))
+    return GQ_EINVAL_PTR;
+  return GQ_OK;
+}
+
+int gq_attn_decode(const void* k_cache, const void* v_cache, int kv_type, int64_t kv_len,
+                   int n_kv_heads, int head_dim, const float* q, int n_heads, float* out,
+                   void* workspace, int64_t workspace_bytes, void* stream) {
+  int64_t need = 0;
+  int rc = check_attn(k_cache, v_cache, kv_type, kv_len, n_kv_heads, head_dim, q, n_heads, out,
+                      &need);
+  if (rc) return rc;
+  if (workspace_bytes < need) return GQ_EINVAL_SHAPE;
+  if (!workspace) return GQ_EINVAL_PTR;
+  if (!aligned16(workspace)) return GQ_EALIGN;
+  const int64_t rb = gq_row_bytes(kv_type, head_dim);
+  const int64_t cbytes = kv_len * n_kv_heads * rb;
+  const int64_t qbytes = (int64_t)n_heads * head_dim * 4;
+  if (overlap(out, qbytes, workspace, need) || overlap(workspace, need, q, qbytes) ||
+      overlap(workspace, need, k_cache, cbytes) || overlap(workspace, need, v_cache, cbytes))
     return GQ_EINVAL_PTR;
   return hip_status(gq::launch_attn_decode(kv_type, k_cache, v_cache, kv_len, n_kv_heads,
                                            head_dim, q, n_heads, out, (float*)workspace,
                                            (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// Workspace of gq_attn_decode_noalloc: a fixed array in device memory.  The
+// runtime gives every GPU the library runs on its own copy when it loads the
+// code object, held until the process ends.  In host code the name is only
+// a stand-in for the symbol: the device address of a GPU's copy comes from
+// hipGetSymbolAddress with that GPU current, looked up once per device.
+constexpr int64_t kScratchBytes = GQ_ATTN_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of device dev's copy of scratch, or null on a HIP error.
+void* scratch_on(int dev) {
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (cur != dev && hipSetDevice(cur) != hipSuccess) return nullptr;
+  if (e != hipSuccess || !addr) return nullptr;
+  g_scratch_ptr[dev].store(addr, std::memory_order_release);
+  return addr;
+}
+}  // namespace
+
+extern "C" {
+
+int gq_attn_decode_noalloc(const void* k_cache, const void* v_cache, int kv_type, int64_t kv_len,
+                           int n_kv_heads, int head_dim, const float* q, int n_heads, float* out,
+                           void* stream) {
+  int64_t need = 0;
+  int rc = check_attn(k_cache, v_cache, kv_type, kv_len, n_kv_heads, head_dim, q, n_heads, out,
+                      &need);
+  if (rc) return rc;
+  if (need > kScratchBytes) return GQ_EOVERFLOW;
+  // the GPU the work runs on: the stream's, or the current one for NULL
+  hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  if ((st ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev)) != hipSuccess) return GQ_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return GQ_EHIP;
+  void* ws = scratch_on(dev);
+  if (!ws) return GQ_EHIP;
+  return hip_status(gq::launch_attn_decode(kv_type, k_cache, v_cache, kv_len, n_kv_heads,
+                                           head_dim, q, n_heads, out, (float*)ws, st));
 }
 
 int gq_probe_stream_read(const void* buf, int64_t bytes, uint32_t* out, void* stream) {

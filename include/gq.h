@@ -240,6 +240,27 @@ int gq_attn_decode(const void *k_cache, const void *v_cache, int kv_type, int64_
                    void *workspace, int64_t workspace_bytes, void *stream);
 
 /*
+ * gq_attn_decode for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and result, with the workspace taken from a fixed
+ * array of GQ_ATTN_NOALLOC_SCRATCH_BYTES in device memory that the library
+ * holds on every GPU it runs on until the process ends.  The call allocates
+ * and frees nothing.  Arguments as for gq_attn_decode without the
+ * workspace; the work runs on the stream's device (the current device for a
+ * NULL stream).  A call whose workspace would exceed the array
+ * (gq_attn_decode_workspace_bytes > GQ_ATTN_NOALLOC_SCRATCH_BYTES) returns
+ * GQ_EOVERFLOW before any HIP call; a failure to find the array's device
+ * address returns GQ_EHIP.  All calls on one GPU share its array: calls that
+ * may overlap in time on one GPU (different streams, or host threads without
+ * ordering) race and must not be issued; calls in one stream are ordered and
+ * safe.  Nothing in the array needs to start at any value.
+ */
+#define GQ_ATTN_NOALLOC_SCRATCH_BYTES (32 << 20)
+int gq_attn_decode_noalloc(const void *k_cache, const void *v_cache, int kv_type,
+                           int64_t kv_len, int n_kv_heads, int head_dim, const float *q,
+                           int n_heads, float *out, void *stream);
+
+/*
  * Measurement: a plain streaming read of `bytes` bytes of device memory at
  * buf with non-temporal 128-bit loads, every byte read once, nothing else done.  Its
  * bandwidth is the practical ceiling the GEMV kernels' effective bandwidth

@@ -155,3 +155,41 @@ def test_matmul_path_validation():
     assert L.gq_matmul_path(*args, 2, -1, None) == -2
     assert L.gq_matmul_path(A, gq.Q4_K, 16, 100, B, gq.F32, 0x30000, 2, gq.PATH_TILED, None) == -2
     assert L.gq_matmul_path(*args, 0, gq.PATH_TILED, None) == 0          # no tokens: no-op
+
+
+def test_attn_kv_cache_bound():
+    """Each KV cache stays within 0x7FFF0000 bytes: out-of-chunk loads go to
+    that offset and must read as zero."""
+    L = gq.lib()
+    K, V, Q, O, WS = 0x100000, 0x200000, 0x300000, 0x310000, 0x400000
+    rb = 136                                                          # q8_0, head_dim 128
+    n_ok = 0x7FFF0000 // (8 * rb)
+    assert L.gq_attn_decode(K, V, gq.Q8_0, n_ok + 1, 8, 128, Q, 8, O, WS, 1 << 40, None) == -5
+
+
+def test_attn_noalloc_validation():
+    """gq_attn_decode_noalloc: the same checks as gq_attn_decode, and a call
+    whose workspace would exceed the fixed array is refused before any HIP
+    call (so all of this runs without a GPU)."""
+    L = gq.lib()
+    K, V, Q, O = 0x100000, 0x200000, 0x300000, 0x310000
+    ok = (K, V, gq.Q8_0, 100, 2, 128, Q, 8, O, None)
+
+    def call(**kw):
+        names = ["k", "v", "t", "n", "nkv", "hd", "q", "nh", "o", "s"]
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return L.gq_attn_decode_noalloc(*[a[n] for n in names])
+
+    assert call(t=gq.Q4_K) == -1
+    assert call(hd=96) == -2 and call(nh=7) == -2
+    assert call(k=None) == -3 and call(o=None) == -3
+    assert call(v=V + 4) == -4
+    assert call(o=Q + 64) == -3
+    # 2^22 positions, one KV head, 16 query heads of 128: 16384 chunks of 256,
+    # 16384 * 16 * 130 * 4 bytes of statistics > the 32 MiB array
+    big = L.gq_attn_decode_workspace_bytes(1 << 22, 1, 16, 128)
+    assert big > (32 << 20)
+    far = dict(k=1 << 40, v=2 << 40, q=3 << 40, o=4 << 40)          # ranges that do not overlap
+    assert call(n=1 << 22, nkv=1, nh=16, **far) == -5
+    assert "gq_attn_decode_noalloc" in gq.header_symbols()
