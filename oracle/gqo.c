@@ -44,6 +44,18 @@
  *     exact), t = a*q (exact) and then one rounding in t - b.  Q6_K forms the
  *     integer k = sc*(q-32) first, then d*k (exact).  The others are d*(q-off)
  *     (exact).  The pages' "-> fp16" comments are not followed: fp32 is used.
+ *  R14 Q4_1 (named only, [NL] list of formats): Q4_0's block with an fp16
+ *     min after the scale: d @0, m @2, qs[16] @4 in Q4_0 nibble order;
+ *     w = d*q + m (the block minimum carried as a signed fp16, so the 16
+ *     levels span [m, m + 15d]: [HG §11.2] item 2's asymmetric range); 20
+ *     bytes per 32 weights = 5.0 bpw.  fp32 order: d*q exact, one rounding
+ *     in d*q + m.
+ *  R15 Q5_K (256-weight super-block at 5.5-5.7 bpw [LC table]): Q4_K's
+ *     fields plus one fifth bit per weight, d @0, dmin @2, scales[12] @4 (R1),
+ *     qh[32] @16, qs[128] @48 (R2); bit e of the 256-bit little-endian qh
+ *     field is bit 4 of element e's code (as Q5_0's qh word, R3); q in
+ *     [0, 31], w = (d*sc_i)*q - dmin*m_i in the fp32 order of R6.  176
+ *     bytes = 5.5 bpw, Q4_K's 4.5 plus the fifth bit.
  *  R13 Quantized KV cache: K and V are each [kv_len][n_kv][head_dim], row
  *     (t, g) = t*n_kv + g quantized along head_dim in blocks of the cache's
  *     type (the page's cache tensor is [batch, positions, kv heads, head
@@ -54,7 +66,10 @@
  *     rounded half away from zero.  A block whose cover would exceed the
  *     largest finite fp16 stores 65504 instead (the pages store every scale as
  *     an fp16, [HG §11.1]; an infinite scale would decode to NaN or Inf), so
- *     its codes clamp at the ends of their range.
+ *     its codes clamp at the ends of their range.  Q4_1: m is the largest
+ *     fp16 <= the block minimum (saturating at -65504), d the cover of
+ *     (max - m)/15, q = clamp(rnd((w - m)/d), 0, 15).  Q5_K: as Q4_K with 31
+ *     levels per sub-block instead of 15.
  */
 #include "gqo.h"
 #include <math.h>
@@ -69,7 +84,9 @@
  *   7 RMSNorm leaves out eps, 8 SiLU uses exp(+v),
  *   9 attention scores without the 1/sqrt(head_dim) scale,
  *   10 query head h reads KV head h % n_kv instead of h / n_rep,
- *   11 a block scale with no finite cover is stored as Inf. */
+ *   11 a block scale with no finite cover is stored as Inf,
+ *   12 Q4_1 min subtracted instead of added,
+ *   13 Q5_K fifth bits read from element e ^ 1. */
 #ifndef GQO_PLANT
 #define GQO_PLANT 0
 #endif
@@ -143,6 +160,8 @@ int gqo_block_info(int type, int64_t *qk, int64_t *bb) {
     case GQO_Q8_0: k = 32;  b = 34;  break;   /* 2 + 32      (R5) */
     case GQO_Q4_K: k = 256; b = 144; break;   /* 2+2+12+128  [HG §11.2, LC] */
     case GQO_Q6_K: k = 256; b = 210; break;   /* 2+16+128+64 (R4) */
+    case GQO_Q4_1: k = 32;  b = 20;  break;   /* 2 + 2 + 16  (R14) */
+    case GQO_Q5_K: k = 256; b = 176; break;   /* 2+2+12+32+128 (R15) */
     default: return -1;
     }
     if (qk) *qk = k;
@@ -163,7 +182,8 @@ static int check(int type, const void *p, int64_t rows, int64_t cols, const void
 /* Unpacks the integer codes of one block into q[] (length QK) and its header
  * fields.  Field meanings per type are given at the top of the file. */
 typedef struct {
-    double d, dmin;        /* fp16 scales as exact doubles; dmin only for Q4_K */
+    double d, dmin;        /* fp16 scales as exact doubles; dmin: Q4_K and Q5_K's
+                              super-min, Q4_1's min m */
     uint16_t d16, dmin16;
     int sc[16], mn[16];    /* Q4_K: 8 scale + 8 min 6-bit fields; Q6_K: 16 int8 scales */
     int q[256];
@@ -194,7 +214,17 @@ static void unpack_block(int type, const uint8_t *b, block_t *o) {
         }
         break;
     }
+    case GQO_Q4_1:                           /* R14 */
+        o->dmin16 = rd16(b + 2);
+        o->dmin = gqo_half_to_double(o->dmin16);
+        for (int j = 0; j < 16; j++) {
+            o->q[j] = b[4 + j] & 0x0F;
+            o->q[j + 16] = b[4 + j] >> 4;
+        }
+        break;
+    case GQO_Q5_K:                           /* R15: Q4_K's fields and a plane of fifth bits */
     case GQO_Q4_K: {
+        const int qs = (type == GQO_Q5_K) ? 48 : 16;
         o->dmin16 = rd16(b + 2);
         o->dmin = gqo_half_to_double(o->dmin16);
         /* R1: 96-bit little-endian stream of 16 six-bit fields */
@@ -209,9 +239,14 @@ static void unpack_block(int type, const uint8_t *b, block_t *o) {
         /* R2 */
         for (int i = 0; i < 8; i++)
             for (int k = 0; k < 16; k++) {
-                uint8_t byte = b[16 + 16 * i + k];
+                uint8_t byte = b[qs + 16 * i + k];
                 o->q[32 * i + k] = (GQO_PLANT == 1) ? byte >> 4 : byte & 0x0F;
                 o->q[32 * i + k + 16] = (GQO_PLANT == 1) ? byte & 0x0F : byte >> 4;
+            }
+        if (type == GQO_Q5_K)                /* R15: bit e of qh, element e */
+            for (int e = 0; e < 256; e++) {
+                int src = (GQO_PLANT == 13) ? (e ^ 1) : e;
+                o->q[e] |= ((b[16 + src / 8] >> (src % 8)) & 1) << 4;
             }
         break;
     }
@@ -243,6 +278,12 @@ static float deq_f32(int type, const block_t *o, int j) {
     case GQO_Q4_0: return d * (float)(o->q[j] - 8);
     case GQO_Q5_0: return d * (float)(o->q[j] - 16);
     case GQO_Q8_0: return d * (float)o->q[j];
+    case GQO_Q4_1: {                                   /* R14 */
+        float t = d * (float)o->q[j];                  /* exact */
+        float m = (float)o->dmin;                      /* exact: fp16 -> fp32 */
+        return (GQO_PLANT == 12) ? t - m : t + m;      /* the one rounding */
+    }
+    case GQO_Q5_K:
     case GQO_Q4_K: {
         int i = j / 32;
         float a = d * (float)o->sc[i];                 /* exact */
@@ -265,6 +306,9 @@ static double deq_f64(int type, const block_t *o, int j) {
     case GQO_Q4_0: return o->d * (double)(o->q[j] - 8);
     case GQO_Q5_0: return o->d * (double)(o->q[j] - 16);
     case GQO_Q8_0: return o->d * (double)o->q[j];
+    case GQO_Q4_1:                             /* R14: d*q + m */
+        return o->d * (double)o->q[j] + ((GQO_PLANT == 12) ? -o->dmin : o->dmin);
+    case GQO_Q5_K:
     case GQO_Q4_K: {                           /* [HG §11.2]: (d*sc)*q - dmin*m */
         int i = j / 32;
         double m = o->dmin * (double)o->mn[i];
@@ -444,6 +488,19 @@ static uint16_t cover_scale(double maxval, double levels) {
     return h;
 }
 
+/* Largest finite fp16 <= v (saturating at -65504); v finite. */
+static uint16_t half_floor(double v) {
+    if (v >= 0.0) {
+        uint16_t h = gqo_half_up(v);
+        if (h > 0x7BFF) return 0x7BFF;
+        if (gqo_half_to_double(h) > v) h--;                /* h > 0 here */
+        return h;
+    }
+    uint16_t h = gqo_half_up(-v);                          /* smallest magnitude >= |v| */
+    if (h > 0x7BFF) h = 0x7BFF;
+    return (uint16_t)(0x8000 | h);
+}
+
 /* Symmetric absmax block: q = clamp(rnd(w/d), -L, L) + off. [HG §11.1] */
 static void quant_sym32(const float *w, int L, int off, uint16_t *d16, int *q) {
     double a = 0.0;
@@ -479,7 +536,28 @@ static void quant_block(int type, const float *w, uint8_t *b) {
         for (int j = 0; j < 16; j++) b[6 + j] = (uint8_t)((q[j] & 15) | ((q[j + 16] & 15) << 4));
         break;
     }
+    case GQO_Q4_1: {      /* min and scale per block (R14, R7) */
+        double lo = INFINITY, hi = -INFINITY;
+        for (int j = 0; j < 32; j++) {
+            double v = (double)w[j];
+            if (v < lo) lo = v;
+            if (v > hi) hi = v;
+        }
+        uint16_t m16 = half_floor(lo);
+        double m = gqo_half_to_double(m16);
+        uint16_t d16 = cover_scale(hi - m, 15.0);
+        double d = gqo_half_to_double(d16);
+        for (int j = 0; j < 32; j++)
+            q[j] = (d == 0.0) ? 0 : clampi(rnd_away(((double)w[j] - m) / d), 0, 15);
+        wr16(b, d16);
+        wr16(b + 2, m16);
+        for (int j = 0; j < 16; j++) b[4 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+        break;
+    }
+    case GQO_Q5_K:        /* as Q4_K with 31 levels and a plane of fifth bits (R15) */
     case GQO_Q4_K: {      /* min/scale, two-level [HG §11.2 items 1-2] */
+        const int L = (type == GQO_Q5_K) ? 31 : 15;
+        const int qs = (type == GQO_Q5_K) ? 48 : 16;
         double hi[8], M[8], Mp[8], sp[8];
         double maxM = 0.0, maxs = 0.0;
         for (int i = 0; i < 8; i++) {
@@ -499,7 +577,7 @@ static void quant_block(int type, const float *w, uint8_t *b) {
         for (int i = 0; i < 8; i++) {
             mn[i] = (dmin == 0.0) ? 0 : clampi(ceil(M[i] / dmin), 0, 63);
             Mp[i] = dmin * (double)mn[i];                 /* >= M[i] */
-            sp[i] = (hi[i] + Mp[i]) / 15.0;
+            sp[i] = (hi[i] + Mp[i]) / (double)L;
             if (sp[i] > maxs) maxs = sp[i];
         }
         uint16_t d16 = cover_scale(maxs, 63.0);
@@ -509,7 +587,7 @@ static void quant_block(int type, const float *w, uint8_t *b) {
             double step = d * (double)sc[i];
             for (int j = 0; j < 32; j++)
                 q[32 * i + j] = (step == 0.0) ? 0
-                    : clampi(rnd_away(((double)w[32 * i + j] + Mp[i]) / step), 0, 15);
+                    : clampi(rnd_away(((double)w[32 * i + j] + Mp[i]) / step), 0, L);
         }
         wr16(b, d16);
         wr16(b + 2, dmin16);
@@ -522,7 +600,9 @@ static void quant_block(int type, const float *w, uint8_t *b) {
         }
         for (int i = 0; i < 8; i++)                       /* R2 */
             for (int k = 0; k < 16; k++)
-                b[16 + 16 * i + k] = (uint8_t)(q[32 * i + k] | (q[32 * i + k + 16] << 4));
+                b[qs + 16 * i + k] = (uint8_t)((q[32 * i + k] & 15) | ((q[32 * i + k + 16] & 15) << 4));
+        if (type == GQO_Q5_K)                             /* R15 */
+            for (int e = 0; e < 256; e++) b[16 + e / 8] |= (uint8_t)(((q[e] >> 4) & 1) << (e % 8));
         break;
     }
     case GQO_Q6_K: {      /* symmetric per 16-weight sub-block, two-level */

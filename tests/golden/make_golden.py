@@ -176,6 +176,65 @@ def q6_k():
     })
 
 
+def q4_1():
+    d, m = Fraction(3, 16), Fraction(-5, 4)
+    codes = [(9 * j + 2) % 16 for j in range(32)]
+    raw = struct.pack("<HH", f16_bits_of(d), f16_bits_of(m) if m >= 0 else
+                      0x8000 | f16_bits_of(-m))
+    raw += bytes(codes[j] | (codes[j + 16] << 4) for j in range(16))
+    assert len(raw) == 20
+    exp = [d * q + m for q in codes]
+    dump("q4_1_min.json", {
+        "type": "q4_1",
+        "citation": "How LLM Inference Engines Work, 'Loading GGUF Models' names Q4_1 "
+                    "among the GGUF formats; the layout is not on the pages. Reading: the "
+                    "Q4_0 block of that section with a signed fp16 min after the fp16 "
+                    "scale (the asymmetric range of Hitchhiker's Guide §11.2 item 2): "
+                    "d, m, then 16 bytes of codes in Q4_0 nibble order; w = d*q + m; "
+                    "20 B per 32 weights = 5.0 bpw.",
+        "fields": {"d": str(d), "m": str(m), "codes": codes},
+        "hex": raw.hex(),
+        "expected": [float(v) for v in exp],
+        "expected_f32": [frac_f32(v) for v in exp],
+    })
+
+
+def q5_k():
+    d, dmin = Fraction(1, 128), Fraction(3, 256)
+    sc = [62 - 7 * i for i in range(8)]
+    mn = [9 * i for i in range(8)]
+    codes = [(13 * j + 7) % 32 for j in range(256)]
+    fields = []
+    for i in range(8):
+        fields += [sc[i], mn[i]]
+    raw = struct.pack("<HH", f16_bits_of(d), f16_bits_of(dmin)) + pack6(fields)
+    qh = 0
+    for e, q in enumerate(codes):
+        qh |= ((q >> 4) & 1) << e
+    raw += qh.to_bytes(32, "little")
+    for i in range(8):
+        for k in range(16):
+            raw += bytes([(codes[32 * i + k] & 15) | ((codes[32 * i + k + 16] & 15) << 4)])
+    assert len(raw) == 176
+    exp = [(d * sc[j // 32]) * codes[j] - dmin * mn[j // 32] for j in range(256)]
+    dump("q5_k_fields.json", {
+        "type": "q5_k",
+        "citation": "12 — llama.cpp / GGUF, table 'Other k-quants at a glance': Q5_K_S / _M "
+                    "at 5.5-5.7 bits per weight over a 256-weight super-block; the layout "
+                    "is not on the pages. Reading: the Q4_K super-block of Hitchhiker's "
+                    "Guide §11.2 (d, dmin, 16 six-bit fields as one LSB-first 96-bit "
+                    "stream, field 2i scale and 2i+1 min of sub-block i) with a 32-byte "
+                    "plane of fifth bits after the fields (bit e of the little-endian "
+                    "256-bit plane is bit 4 of element e's code, as Q5_0's 32-bit word), "
+                    "then the 128 code bytes in Q4_0 nibble order per sub-block; "
+                    "w = (d*sc)*q - dmin*m with q in 0..31; 176 B = 5.5 bpw.",
+        "fields": {"d": str(d), "dmin": str(dmin), "sc": sc, "m": mn, "codes": codes},
+        "hex": raw.hex(),
+        "expected": [float(v) for v in exp],
+        "expected_f32": [frac_f32(v) for v in exp],
+    })
+
+
 if __name__ == "__main__":
     q4_0()
     q8_0()
@@ -192,3 +251,5 @@ if __name__ == "__main__":
          "Extreme fields: d = 1.0, dmin = 2^-14 * 1025/1024, so the single fp32 "
          "rounding of a*q - b is exercised.")
     q6_k()
+    q4_1()
+    q5_k()

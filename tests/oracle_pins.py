@@ -32,7 +32,7 @@ import numpy as np
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-QTYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k"]
+QTYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k"]
 
 
 def golden_fixtures():
@@ -72,6 +72,11 @@ def pin_sizes(o):
     # Q8_0 (Q4_0 structure, 8-bit codes) and Q5_0 (4+1 bit codes).
     assert o.block_info("q8_0") == (32, 2 + 32)
     assert o.block_info("q5_0") == (32, 2 + 4 + 16)
+    # Q4_1: Q4_0's block plus an fp16 min (5.0 bpw); Q5_K: Q4_K plus one fifth
+    # bit per weight, 5.5 bpw, inside the table's 5.5-5.7 for Q5_K_S / _M.
+    assert o.block_info("q4_1") == (32, 2 + 2 + 16)
+    qk, bb = o.block_info("q5_k")
+    assert qk == 256 and bb == 144 + 256 // 8 and 5.5 <= bb * 8 / qk <= 5.7
 
 
 def _exact_dot(w64, x):
@@ -149,7 +154,8 @@ def pin_q4k_structured(o):
 
 def pin_pow2_and_perm(o):
     """Doubling d (and dmin) doubles y exactly; permuting rows permutes y."""
-    offs = {"q4_0": [0], "q5_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0]}
+    offs = {"q4_0": [0], "q5_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "q4_1": [0, 2],
+            "q5_k": [0, 2]}
     for k, t in enumerate(QTYPES):
         qk, bb = o.block_info(t)
         rows, cols = 6, 2 * qk
@@ -207,13 +213,20 @@ def _roundtrip_bound(w: np.ndarray, t: str) -> np.ndarray:
         d = ts.max(axis=1, keepdims=True) / 127.0 * up + 2.0 ** -24             # [blocks,1,1]
         step = ts + d
         return np.broadcast_to(step / 2, (ts.shape[0], 16, 16)).reshape(w.shape)
-    # q4_k
+    if t == "q4_1":
+        b = w.reshape(-1, 32)
+        lo, hi = b.min(axis=1, keepdims=True), b.max(axis=1, keepdims=True)
+        span = (hi - lo) + np.abs(lo) * 2.0 ** -10 + 2.0 ** -24      # m is an fp16 <= lo
+        d = span / 15.0 * up + 2.0 ** -24
+        return np.broadcast_to(d / 2, b.shape).reshape(w.shape)
+    # q4_k, q5_k
+    L = 31.0 if t == "q5_k" else 15.0
     sb = w.reshape(-1, 8, 32)
     lo = np.minimum(sb.min(axis=2), 0.0)
     hi = sb.max(axis=2)
     M = -lo
     dmin = M.max(axis=1, keepdims=True) / 63.0 * up + 2.0 ** -24
-    sp = (hi + M + dmin) / 15.0
+    sp = (hi + M + dmin) / L
     d = sp.max(axis=1, keepdims=True) / 63.0 * up + 2.0 ** -24
     step = sp + d
     return np.broadcast_to((step / 2)[..., None], sb.shape).reshape(w.shape)
@@ -251,7 +264,7 @@ def pin_quantize_saturation(o):
     times the largest magnitude the type can represent."""
     top = 65504.0
     big = {"q4_0": top * 7, "q5_0": top * 15, "q8_0": top * 127, "q6_k": top * 127 * 31,
-           "q4_k": top * 63 * 15}
+           "q4_k": top * 63 * 15, "q5_k": top * 63 * 31, "q4_1": top * 16}
     for t in QTYPES:
         qk, _ = o.block_info(t)
         ramp = np.linspace(-1.0, 1.0, qk)
@@ -260,11 +273,16 @@ def pin_quantize_saturation(o):
         assert _f16_field(blob, 0) == 0x7BFF, (t, hex(_f16_field(blob, 0)))
         w64 = o.dequant_f64(blob, t, 1, qk)[0]
         assert np.all(np.isfinite(w64)), t
-        if t == "q4_k":
+        if t in ("q4_k", "q5_k"):
             assert _f16_field(blob, 2) == 0x7BFF, (t, "dmin")
             # sub-block 0 all negative: code 0 at min 63; sub-block 7 all
-            # positive: code 15 at scale 63, min 0
-            assert w64[0] == -top * 63 and w64[-1] == top * 63 * 15, (t, w64[0], w64[-1])
+            # positive: the top code at scale 63, min 0
+            top_code = 31 if t == "q5_k" else 15
+            assert w64[0] == -top * 63 and w64[-1] == top * 63 * top_code, (t, w64[0], w64[-1])
+        elif t == "q4_1":
+            # the min saturates at -65504 (0xFBFF), codes 0 and 15 at the ends
+            assert _f16_field(blob, 2) == 0xFBFF, (t, hex(_f16_field(blob, 2)))
+            assert w64[0] == -top and w64[-1] == 14 * top, (t, w64[0], w64[-1])
         elif t == "q6_k":
             assert int(blob[2]) == 127 and int(blob[2 + 15]) == 127, t      # scales clamp at 127
             assert w64[0] == -big[t] and w64[-1] == big[t], t

@@ -17,7 +17,8 @@ PLANTS = {1: "nibble order swapped", 2: "Q4_K min sign", 3: "Q4_K scale/min swap
           4: "Q6_K offset", 5: "dot drops a column", 6: "dot reads x transposed",
           7: "RMSNorm drops eps", 8: "SiLU exponent sign",
           9: "attention without 1/sqrt(head_dim)", 10: "attention head mapping h % n_kv",
-          11: "unsaturated (Inf) block scale"}
+          11: "unsaturated (Inf) block scale", 12: "Q4_1 min sign",
+          13: "Q5_K fifth bits of the neighbouring element"}
 
 
 @pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda k: PLANTS[k])
