@@ -262,10 +262,31 @@ def gemm_fetch_from_profile():
     return float(m_b.group(1))
 
 
+def cpu_threads():
+    """Threads for the CPU oracle: every core of the affinity mask, within the
+    host's CPU share for this GPU when the environment states one
+    (OMP_NUM_THREADS); returns (threads, affinity cores)."""
+    aff = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    th = min(aff, int(share)) if share.isdigit() and int(share) > 0 else aff
+    return max(1, th), aff
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(layer_mats):
     import numpy as np
     import oracle
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    threads, aff = cpu_threads()
     work = []
     for m in layer_mats:
         blob = np.concatenate([oracle.quantize(w, m.t) for w in m.w])   # the oracle's own blobs
@@ -284,23 +305,52 @@ def cpu_baseline(layer_mats):
             ts.append(time.perf_counter() - t0)
         res[th] = float(np.median(ts))
         reps[th] = len(ts)
-    cpu = "unknown"
-    try:
-        with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
     return {
         "value": round(total / res[threads] / 1e9, 3), "unit": "GB/s", "cores": threads,
         "kind": "oracle",
         "sample": f"the whole layer (4 matrices, {total} blob bytes) per repetition, fp64 "
-                  f"dequant-then-dot, median of {reps[threads]} repetitions on {threads} threads; "
+                  f"dequant-then-dot, median of {reps[threads]} repetitions on {threads} threads "
+                  f"({aff} cores in the affinity mask, {threads} the host's share for this GPU); "
                   f"1 thread: {round(total / res[1] / 1e9, 3)} GB/s (median of {reps[1]}, "
-                  f"{res[1]:.2f} s each); CPU: {cpu}",
+                  f"{res[1]:.2f} s each); CPU: {cpu_model()}",
     }
+
+
+def cpu_baselines():
+    """The CPU oracle on every workload configuration (bounded samples of
+    rows, all tokens, about one second each on all threads): the single
+    2048x2048 Q4_K GEMV, the per-type 4096x4096 sweep and the 32000x4096 Q6_K
+    head, Q4_K 11008x4096 at 1, 8 and 64 fp16 tokens, and the Llama-3-8B layer
+    set at 1, 8 and 64 tokens.  GB/s = blob bytes of the sampled rows / time;
+    GFLOP/s = 2 * sampled rows * cols * tokens / time."""
+    import numpy as np
+    import oracle
+    import synth
+    threads, _ = cpu_threads()
+    cases = [("single q4_k 2048x2048 n=1", "q4_k", 2048, 2048, 1, "f32")]
+    cases += [(f"per-type {t} {r}x{c} n=1", t, r, c, 1, "f32") for _, t, r, c in synth.PER_TYPE_SWEEP_4096]
+    cases += [(f"q4_k 11008x4096 n={n} f16", "q4_k", 11008, 4096, n, "f16") for n in (1, 8, 64)]
+    for n in synth.LLAMA3_8B_TOKENS:
+        for name, t, r, c in synth.LLAMA3_8B_LAYER_Q4KM:
+            cases.append((f"llama3-8b {name} {t} {r}x{c} n={n}", t, r, c, n, "f32" if n == 1 else "f16"))
+    out = []
+    for i, (label, t, rows, cols, n, xdt) in enumerate(cases):
+        # rows sampled so one repetition is ~30 M fp64 multiply-adds
+        sr = int(min(rows, max(64, 30e6 // (cols * max(n, 4)))))
+        w = synth.weights(sr, cols, seed=9500 + i)
+        blob = oracle.quantize(w, t)
+        x = synth.activations(n, cols, seed=9600 + i, dtype=xdt)
+        ts = []
+        t_start = time.perf_counter()
+        while len(ts) < 3 or time.perf_counter() - t_start < 0.8:
+            t0 = time.perf_counter()
+            oracle.matmul_f64(blob, t, sr, cols, x, threads=threads)
+            ts.append(time.perf_counter() - t0)
+        tm = float(np.median(ts))
+        out.append({"case": label, "rows_sampled": sr, "GBps": round(blob.size / tm / 1e9, 3),
+                    "GFLOPs": round(2.0 * sr * cols * n / tm / 1e9, 2), "threads": threads})
+        log(f"  cpu {label}: {sr} rows, {out[-1]['GBps']} GB/s, {out[-1]['GFLOPs']} GFLOP/s")
+    return out
 
 
 def cpu_baseline_gemm(threads=None):
@@ -312,7 +362,7 @@ def cpu_baseline_gemm(threads=None):
     import numpy as np
     import oracle
     import synth
-    threads = threads or max(1, min(16, len(os.sched_getaffinity(0))))
+    threads = threads or cpu_threads()[0]
     rows, cols, n = 688, 4096, 512
     w = synth.weights(rows, cols, seed=9000)
     blob = oracle.quantize(w, "q4_k")
@@ -337,6 +387,9 @@ def sweep(steps):
     cases = [("single q4_k 2048x2048", "q4_k", [("w", 2048)], 2048, 1, "f32")]
     cases += [(f"per-type {t} {r}x{c}", t, [(n, r)], c, 1, "f32") for n, t, r, c in synth.PER_TYPE_SWEEP_4096]
     cases += [(f"q4_k 11008x4096 n={n} f16", "q4_k", [("w", 11008)], 4096, n, "f16") for n in synth.GEMM_TOKENS]
+    for t in ("q4_1", "q5_k"):
+        cases += [(f"{t} 4096x4096 n=1", t, [("w", 4096)], 4096, 1, "f32"),
+                  (f"{t} 4096x4096 n=512 f16", t, [("w", 4096)], 4096, 512, "f16")]
     for n in synth.LLAMA3_8B_TOKENS:
         for name, t, r, c in synth.LLAMA3_8B_LAYER_Q4KM:
             cases.append((f"llama3-8b {name} {t} {r}x{c} n={n}", t, [(name, r)], c, n, "f32" if n == 1 else "f16"))
@@ -344,10 +397,17 @@ def sweep(steps):
         m = Mat(label, t, parts, cols, seed=9000 + 31 * i, ncopies=1, n_tok=n, x_dtype=xdt)
         ms = kernel_time_ms(m, max(64, steps // 2), per_graph=8 if m.bytes > (64 << 20) else 16)
         flops = 2.0 * m.rows * cols * n
+        gbps = m.bytes / (ms * 1e-3) / 1e9
+        tfl = flops / (ms * 1e-3) / 1e12
+        # the roofline this shape sits under: fp16 matrix peak once the
+        # flops per weight byte pass the ridge (peak flops / peak bandwidth)
+        mfma = flops / m.bytes > FP16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
         out.append({"case": label, "blob_bytes": m.bytes, "us": round(ms * 1e3, 2),
-                    "GBps": round(m.bytes / (ms * 1e-3) / 1e9, 1),
-                    "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2)})
-        log(f"  {label}: {ms*1e3:.2f} us  {out[-1]['GBps']} GB/s  {out[-1]['TFLOPs']} TFLOP/s")
+                    "GBps": round(gbps, 1), "TFLOPs": round(tfl, 2),
+                    "bound": "mfma" if mfma else "hbm",
+                    "frac": round(tfl / FP16_PEAK_TFLOPS if mfma else gbps / HBM_PEAK_GBS, 4)})
+        log(f"  {label}: {ms*1e3:.2f} us  {out[-1]['GBps']} GB/s  {out[-1]['TFLOPs']} TFLOP/s "
+            f"({out[-1]['bound']} {out[-1]['frac']})")
         del m
     return out
 
@@ -583,10 +643,13 @@ def main():
         log("attention decode over quantized KV caches")
         attn = attn_bench(args.steps)
 
-    cpu = None
+    cpu, cpus = None, None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         cpu = cpu_baseline(mats)
+        if not args.no_sweep:
+            log("cpu baselines of the other workload configurations (oracle, row samples)")
+            cpus = cpu_baselines()
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
@@ -604,6 +667,7 @@ def main():
         "fused_layer": fused,
         "per_launch": per,
         "sweep": shapes,
+        "cpu_baselines": cpus,
     }
     print(json.dumps(out), flush=True)
 

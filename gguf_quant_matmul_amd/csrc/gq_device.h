@@ -114,6 +114,8 @@ template <> struct Geo<GQ_Q5_0> { static constexpr int QK = 32,  BB = 22;  };
 template <> struct Geo<GQ_Q8_0> { static constexpr int QK = 32,  BB = 34;  };
 template <> struct Geo<GQ_Q4_K> { static constexpr int QK = 256, BB = 144; };
 template <> struct Geo<GQ_Q6_K> { static constexpr int QK = 256, BB = 210; };
+template <> struct Geo<GQ_Q4_1> { static constexpr int QK = 32,  BB = 20;  };
+template <> struct Geo<GQ_Q5_K> { static constexpr int QK = 256, BB = 176; };
 
 // A "segment" is 32 consecutive weights of a row: one block of the 32-weight
 // types, one sub-block of Q4_K, one 32-weight group of Q6_K.  Segment s of a
@@ -148,6 +150,31 @@ __device__ __forceinline__ uint32_t q6k_hi(uint32_t hq, int u) {
 __device__ __forceinline__ uint32_t spread4_bit4(uint32_t v) {
   v &= 0xFu;
   return ((v & 1u) << 4) | ((v & 2u) << 11) | ((v & 4u) << 18) | ((v & 8u) << 25);
+}
+
+// Bit b (b = 0..3) of v4 to bit 4 of byte b: the multiply places bit b at
+// bits b + 7k (k = 0..3), all distinct, so no carries; bit 8b is the k = b copy.
+__device__ __forceinline__ uint32_t bits_to_b4(uint32_t v4) {
+  return (((v4 & 0xFu) * 0x00204081u) & 0x01010101u) << 4;   // a 24-bit multiply
+}
+
+// fp16 pair {RNE_fp16(c0 s + nb), RNE_fp16(c1 s + nb)} for codes held in
+// 16-bit fields (c0 in field H of p0, c1 in field H of p1) and a scale s
+// carrying a factor 2^24: a field below 1024 read as fp16 is the subnormal
+// c * 2^-24 exactly, so each v_fma_mix forms the exact c * (s 2^-24) + nb and
+// rounds it once, as the convert-then-mix form does, with no convert.
+template <int H>
+__device__ __forceinline__ uint32_t mixpair(uint32_t p0, uint32_t p1, float s, float nb) {
+  uint32_t d;
+  if constexpr (H == 0)
+    asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel_hi:[1,0,0]"
+        : "=&v"(d) : "v"(p0), "v"(p1), "v"(s), "v"(nb));
+  else
+    asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+        : "=&v"(d) : "v"(p0), "v"(p1), "v"(s), "v"(nb));
+  return d;
 }
 
 // Wave-uniform value in a scalar register.

@@ -67,25 +67,6 @@ __device__ __forceinline__ uint32_t h2pack(float a, float b) {
   return __builtin_bit_cast(uint32_t, h2{(_Float16)a, (_Float16)b});
 }
 
-// fp16 pair {RNE_fp16(c0 s + nb), RNE_fp16(c1 s + nb)} for codes held in
-// 16-bit fields (c0 in field H of p0, c1 in field H of p1) and a scale s
-// carrying a factor 2^24: a field below 1024 read as fp16 is the subnormal
-// c * 2^-24 exactly, so each v_fma_mix forms the exact c * (s 2^-24) + nb and
-// rounds it once, as the convert-then-mix form does, with no convert.
-template <int H>
-__device__ __forceinline__ uint32_t mixpair(uint32_t p0, uint32_t p1, float s, float nb) {
-  uint32_t d;
-  if constexpr (H == 0)
-    asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel_hi:[1,0,0]"
-        : "=&v"(d) : "v"(p0), "v"(p1), "v"(s), "v"(nb));
-  else
-    asm("v_fma_mixlo_f16 %0, %1, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mixhi_f16 %0, %2, %3, %4 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-        : "=&v"(d) : "v"(p0), "v"(p1), "v"(s), "v"(nb));
-  return d;
-}
-
 // ---------------------------------------------------------------------------
 // Weights.  Thread (row r, half h) owns 32 columns of its row per K step: the
 // "segment" sg = 2 * step + h (one Q4_K sub-block, one Q6_K group of 32, one
@@ -122,6 +103,76 @@ template <> struct BR<GQ_Q4_K> {
       const uint32_t e1 = w1 & m, o1 = (w1 >> 8) & m;
       out[c] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
                      mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
+    }
+  }
+};
+// Q5_K: Q4_K's header, the segment's 32 fifth bits, its 16 code bytes; the
+// fifth bit of each code is spread into its 16-bit field (bit 4, or bit 8
+// for high nibbles, which sit in place as 16 q) by a multiply that places
+// bits 0 and 2 of a 4-bit group at both fields at once.
+template <> struct BR<GQ_Q5_K> {
+  static constexpr bool kHeader = true;
+  u32x4 hd, q;
+  uint32_t qh;
+  template <bool HDR = true>
+  __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
+    const int vo = ok ? vrow + (sg >> 3) * 176 : kOobOff;
+    if constexpr (HDR) hd = bld16(R, vo, 0);
+    qh = bld4(R, vo + 4 * (sg & 7), 16);
+    q = bld16(R, vo + 16 * (sg & 7), 48);
+  }
+  __device__ static float bound(const u32x4& hd) {          // 63 * 31 |d| + 63 |dmin|
+    return fmaf(1953.f, fabsf(h2f(hd.x)), 63.f * fabsf(h2f(hd.x >> 16)));
+  }
+  __device__ float bound() const { return bound(hd); }
+  __device__ void decode(int sg, int k, u32x4 out[4]) const { decode(sg, hd, k, out); }
+  __device__ void decode(int sg, const u32x4& hd, int k, u32x4 out[4]) const {
+    const float d = __builtin_ldexpf(h2f(hd.x), k), dmin = __builtin_ldexpf(h2f(hd.x >> 16), k);
+    const uint32_t f = q4k_pair(hd.y, hd.z, hd.w, sg & 7);
+    const float a = d * (float)(f & 63u), nb = -(dmin * (float)(f >> 6));
+    const float a24 = a * 16777216.f, a20 = a * 1048576.f;
+#pragma unroll
+    for (int c = 0; c < 4; c++) {            // chunk c: elements 8c .. 8c+7
+      const uint32_t m = (c < 2) ? 0x000F000Fu : 0x00F000F0u;
+      const float s = (c < 2) ? a24 : a20;
+      // bits 0, 2 of a 4-bit group to bits 4, 20 (low nibbles) or 8, 24 (high)
+      const uint32_t mul = (c < 2) ? 0x00040010u : 0x00400100u;
+      const uint32_t pos = (c < 2) ? 0x00100010u : 0x01000100u;
+      const uint32_t hb = qh >> (8 * c);      // fifth bits of elements 8c .. 8c+7
+      const uint32_t w0 = q[2 * (c & 1)], w1 = q[2 * (c & 1) + 1];
+      const uint32_t e0 = (w0 & m) | (((hb & 5u) * mul) & pos);
+      const uint32_t o0 = ((w0 >> 8) & m) | ((((hb >> 1) & 5u) * mul) & pos);
+      const uint32_t e1 = (w1 & m) | ((((hb >> 4) & 5u) * mul) & pos);
+      const uint32_t o1 = ((w1 >> 8) & m) | ((((hb >> 5) & 5u) * mul) & pos);
+      out[c] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
+                     mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
+    }
+  }
+};
+// Q4_1: one 20-byte block per segment (d | m, 16 code bytes); B = RNE_fp16 of
+// (d q + m) 2^k formed exactly by the mixed FMA.
+template <> struct BR<GQ_Q4_1> {
+  static constexpr bool kHeader = false;
+  u32x4 a;                                   // d | m, code bytes 0..11
+  uint32_t t;                                // code bytes 12..15
+  template <bool HDR = true>
+  __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
+    const int vo = ok ? vrow + sg * 20 : kOobOff;
+    a = bld16(R, vo, 0);
+    t = bld4(R, vo, 16);
+  }
+  __device__ float bound() const { return fmaf(15.f, fabsf(h2f(a.x)), fabsf(h2f(a.x >> 16))); }
+  __device__ void decode(int, int k, u32x4 out[4]) const {
+    const float s = __builtin_ldexpf(h2f(a.x), k + 24), nb = __builtin_ldexpf(h2f(a.x >> 16), k);
+    const uint32_t c[4] = {a.y, a.z, a.w, t};
+#pragma unroll
+    for (int cc = 0; cc < 4; cc++) {         // low nibbles for elements < 16
+      const int sh = 4 * (cc >> 1);
+      const uint32_t w0 = c[2 * (cc & 1)] >> sh, w1 = c[2 * (cc & 1) + 1] >> sh;
+      const uint32_t e0 = w0 & 0x000F000Fu, o0 = (w0 >> 8) & 0x000F000Fu;
+      const uint32_t e1 = w1 & 0x000F000Fu, o1 = (w1 >> 8) & 0x000F000Fu;
+      out[cc] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
+                      mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
     }
   }
 };
@@ -378,7 +429,7 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
       U = b.bound();
     }
     // 32-weight types: the row's two lanes hold different blocks
-    if constexpr (T != GQ_Q4_K && T != GQ_Q6_K) U = max_xor32(U);
+    if constexpr (Geo<T>::QK == 32) U = max_xor32(U);
     if (U > 0.f && U < __builtin_huge_valf()) {
       const int e = fexp(U);
       if (kr == KNONE) kr = 10 - e;         // the products so far are all zero
@@ -547,7 +598,8 @@ double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok) {
       {1.05, 1.75, 1.4, 1.2}, {0.9, 1.3, 1.2, 1.0}, {0.57, 0.95, 0.7, 0.5}};
   static const int64_t bn[3] = {256, 128, 128}, bm[3] = {128, 128, 64}, slots[3] = {256, 512, 768};
   const int c = gemm_tile_config(rows, n_tok);
-  const int tc = (type == GQ_Q4_K) ? 0 : (type == GQ_Q6_K) ? 1 : (type == GQ_Q4_0) ? 3 : 2;
+  const int tc = (type == GQ_Q4_K) ? 0 : (type == GQ_Q6_K || type == GQ_Q5_K) ? 1
+                 : (type == GQ_Q4_0) ? 3 : 2;
   const int64_t tiles = (rows + bn[c] - 1) / bn[c] * ((n_tok + bm[c] - 1) / bm[c]);
   return (double)((tiles + slots[c] - 1) / slots[c]) * (double)((cols + BK - 1) / BK) *
          step_us[c][tc];
@@ -565,6 +617,8 @@ hipError_t launch_gemm(int type, const void* blob, int64_t rows, int64_t cols, c
     GQ_GEMM_CASE(GQ_Q8_0)
     GQ_GEMM_CASE(GQ_Q4_K)
     GQ_GEMM_CASE(GQ_Q6_K)
+    GQ_GEMM_CASE(GQ_Q4_1)
+    GQ_GEMM_CASE(GQ_Q5_K)
 #undef GQ_GEMM_CASE
   }
   return hipErrorInvalidValue;

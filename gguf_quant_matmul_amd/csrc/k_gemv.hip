@@ -218,6 +218,88 @@ template <int T> struct SliceQ40Q50 {
 template <> struct Slice<GQ_Q4_0> : SliceQ40Q50<GQ_Q4_0> {};
 template <> struct Slice<GQ_Q5_0> : SliceQ40Q50<GQ_Q5_0> {};
 
+// acc + w0 x[0] + w1 x[1] + w2 x[2] + w3 x[3] with w_i = RNE_fp32(c_i a + m)
+// exactly the stated dequant of codes c_i (16-bit fields: c0, c2 in p02, c1,
+// c3 in p13, read as the fp16 subnormals c 2^-24) for a scale a24 = a 2^24:
+// one mixed FMA forms each weight with its single rounding, one FMA
+// multiplies it into the sum, so every product carries only its own
+// rounding.
+__device__ __forceinline__ float dot4w(uint32_t p02, uint32_t p13, float a24, float m, const float* x,
+                                       float acc) {
+  float w0, w1, w2, w3;
+  asm("v_fma_mix_f32 %0, %4, %6, %7 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %1, %5, %6, %7 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %2, %4, %6, %7 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mix_f32 %3, %5, %6, %7 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3)
+      : "v"(p02), "v"(p13), "v"(a24), "v"(m));
+  acc = fmaf(w0, x[0], acc);
+  acc = fmaf(w1, x[1], acc);
+  acc = fmaf(w2, x[2], acc);
+  return fmaf(w3, x[3], acc);
+}
+
+// Q4_1 (blocks 2 sl, 2 sl + 1): fp16 d, fp16 m, 16 code bytes in Q4_0 order;
+// each weight d q + m is formed exactly as stated, then multiplied.
+template <> struct Slice<GQ_Q4_1> {
+  u32x4 a0, a1;                              // bytes 0..15 of each block
+  uint32_t t0, t1;                           // bytes 16..19
+  static __device__ int voff(int sl) { return sl * 40; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int) {
+    a0 = bld16(r, vo, 0);
+    t0 = bld4(r, vo, 16);
+    a1 = bld16(r, vo, 20);
+    t1 = bld4(r, vo, 36);
+  }
+  template <bool ASM>
+  __device__ float dot(int h, const float* x, const float*, int) const {
+    const u32x4 A = h ? a1 : a0;
+    const uint32_t c[4] = {A.y, A.z, A.w, h ? t1 : t0};   // code bytes 0..15
+    const float a24 = h2f(A.x) * kSub, m = h2f(A.x >> 16);
+    float s = 0.f, t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {            // low nibbles: elements 4k.., high: 16+4k..
+      const uint32_t u = c[k] >> 8;
+      s = dot4w(c[k] & 0x000F000Fu, u & 0x000F000Fu, a24, m, x + 4 * k, s);
+      t = dot4w((c[k] >> 4) & 0x000F000Fu, (u >> 4) & 0x000F000Fu, a24, m, x + 16 + 4 * k, t);
+    }
+    return s + t;
+  }
+};
+
+// Q5_K (sub-blocks 2j, 2j+1): Q4_K's header, 8 bytes of fifth bits for the
+// slice's 64 elements, 5-bit codes as bytes; factored sub-block sums as Q4_K.
+template <> struct Slice<GQ_Q5_K> {
+  u32x4 hd, q0, q1;
+  u32x2 qh;
+  static __device__ int voff(int sl) { return (sl >> 2) * 176; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int j) {
+    hd = bld16(r, vo, 0);
+    qh = bld8(r, vo + 8 * j, 16);
+    q0 = bld16(r, vo + 32 * j, 48);
+    q1 = bld16(r, vo + 32 * j, 64);
+  }
+  template <bool ASM>
+  __device__ float dot(int h, const float* x, const float* xs, int j) const {
+    const u32x4 q = h ? q1 : q0;              // sub-block 2j + h
+    const uint32_t W = h ? qh.y : qh.x;       // its fifth bits, bit e = element e
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const uint32_t lo = (q[k] & 0x0F0F0F0Fu) | bits_to_b4(W >> (4 * k));
+      const uint32_t hi = ((q[k] >> 4) & 0x0F0F0F0Fu) | bits_to_b4(W >> (16 + 4 * k));
+      s = dot4u_asm(lo, x + 4 * k, s);
+      s = dot4u_asm(hi, x + 16 + 4 * k, s);
+    }
+    const uint32_t lo = (j <= 1) ? hd.y : (j == 2) ? hd.z : hd.w;
+    const uint32_t hi = (j <= 1) ? hd.z : hd.w;
+    const uint32_t f = __builtin_amdgcn_alignbit(hi, lo, (24 * j) & 31) >> (12 * h);
+    const float a = h2f(hd.x) * (float)(f & 63u);
+    const float b = h2f(hd.x >> 16) * (float)((f >> 6) & 63u);
+    return fmaf(a, s, -b * (xs[0] + xs[1]));
+  }
+};
+
 // Physical float index in LDS of logical x index f: 16-byte chunk c of slice
 // s lands at chunk c ^ (s & 15), so 16 lanes reading chunk c of 16
 // consecutive slices hit 16 distinct groups of 4 banks.
@@ -552,6 +634,8 @@ hipError_t launch_gemv_fused(int type, const void* blob, const void* up_blob, in
     case GQ_Q8_0: return gemv_t<GQ_Q8_0>(blob, rows, cols, x, x_f16, y, fu, st);
     case GQ_Q4_K: return gemv_t<GQ_Q4_K>(blob, rows, cols, x, x_f16, y, fu, st);
     case GQ_Q6_K: return gemv_t<GQ_Q6_K>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q4_1: return gemv_t<GQ_Q4_1>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q5_K: return gemv_t<GQ_Q5_K>(blob, rows, cols, x, x_f16, y, fu, st);
   }
   return hipErrorInvalidValue;
 }

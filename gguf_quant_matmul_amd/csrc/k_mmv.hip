@@ -158,6 +158,17 @@ template <> struct WS<GQ_Q4_K> {     // slab = one super-block; sub-blocks 2g, 2
   }
 };
 
+template <> struct WS<GQ_Q5_K> {     // Q4_K's share plus the 64 fifth bits
+  u32x4 hd, q[2];
+  u32x2 qh;
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int g) {
+    hd = bld16(r, vo, 0);
+    qh = bld8(r, vo + 8 * g, 16);
+    q[0] = bld16(r, vo + 32 * g, 48);
+    q[1] = bld16(r, vo + 32 * g, 64);
+  }
+};
+
 template <> struct WS<GQ_Q6_K> {     // slab = one super-block; 32-groups 2g, 2g+1
   u32x4 l[2], h;
   uint32_t sc4, d;
@@ -234,15 +245,45 @@ __device__ __forceinline__ void stage_w(uint8_t* ww, const WS32<T>& ws, int r, i
   *reinterpret_cast<uint32_t*>(ww + W::WD + r * 16 + 4 * g) = dd;
 }
 
+// Q4_1: blocks are 20 dword-aligned bytes (d | m, then 16 code bytes), each
+// loaded as 16 + 4 bytes and staged as codes [16][8][16], d [16][8] fp16 and
+// m [16][8] fp16.
+struct WSQ41 {
+  static constexpr int CB = 16, WD = 16 * 8 * 16, WQ = WD + 256, WBYTES = WQ + 256;
+  uint32_t raw[2][5];
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo) {
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      const u32x4 v = bld16(r, vo + 20 * b, 0);
+      raw[b][0] = v.x; raw[b][1] = v.y; raw[b][2] = v.z; raw[b][3] = v.w;
+      raw[b][4] = bld4(r, vo + 20 * b, 16);
+    }
+  }
+};
+template <> constexpr int kWB<GQ_Q4_1> = WSQ41::WBYTES;
+template <> struct WS<GQ_Q4_1> : WSQ41 {};
+
+__device__ __forceinline__ void stage_w_q41(uint8_t* ww, const WSQ41& ws, int r, int g, bool ok_a,
+                                            bool ok_b) {
+  uint8_t* const c = ww + r * 8 * 16 + 2 * g * 16;
+  uint32_t dd = 0, mm = 0;
+#pragma unroll
+  for (int b = 0; b < 2; b++) {
+    const uint32_t* D = ws.raw[b];
+    *reinterpret_cast<u32x4*>(c + 16 * b) = u32x4{D[1], D[2], D[3], D[4]};
+    if (b ? ok_b : ok_a) {                    // blocks past the row's end: d = m = 0
+      dd |= (D[0] & 0xFFFFu) << (16 * b);
+      mm |= (D[0] >> 16) << (16 * b);
+    }
+  }
+  *reinterpret_cast<uint32_t*>(ww + WSQ41::WD + r * 16 + 4 * g) = dd;
+  *reinterpret_cast<uint32_t*>(ww + WSQ41::WQ + r * 16 + 4 * g) = mm;
+}
+
 template <> struct WS<GQ_Q4_0> : WS32<GQ_Q4_0> {};
 template <> struct WS<GQ_Q5_0> : WS32<GQ_Q5_0> {};
 template <> struct WS<GQ_Q8_0> : WS32<GQ_Q8_0> {};
 
-// Bit b (b = 0..3) of v4 to bit 4 of byte b: the multiply places bit b at
-// bits b + 7k (k = 0..3), all distinct, so no carries; bit 8b is the k = b copy.
-__device__ __forceinline__ uint32_t bits_to_b4(uint32_t v4) {
-  return (((v4 & 0xFu) * 0x00204081u) & 0x01010101u) << 4;   // a 24-bit multiply
-}
 
 // 16-token matrix-op tiles per pass: one for P = 8 or 16, two for P = 32
 // (each decoded B fragment then feeds both tiles).
@@ -270,7 +311,7 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, c
   constexpr int MT = kMT<P>;
   const f32x4v z = {0.f, 0.f, 0.f, 0.f};
   const f32x4 iv = inv_scales<XLO, P>(sv, g);   // fp32 x: undo the slab's scale
-  if constexpr (T == GQ_Q4_K) {
+  if constexpr (T == GQ_Q4_K || T == GQ_Q5_K) {
     const float d = h2f(ws.hd.x), dmin = h2f(ws.hd.x >> 16);
     f16x8 M[2];
     f16x2 SL[2], NL[2], SH[2], NH[2];
@@ -292,10 +333,21 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, c
     for (int j = 0; j < 8; j++) {
       const int h = j >> 2, qq = j & 3;       // sub-block 2g + h, eighth qq
       const uint32_t D0 = ws.q[h][2 * (qq & 1)], D1 = ws.q[h][2 * (qq & 1) + 1];
-      const uint32_t msk = (qq < 2) ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
       f16x2 v[4];
-      bytes8(kE1024, D0 & msk, D1 & msk, v);
-      const f16x2 s = (qq < 2) ? SL[h] : SH[h], n = (qq < 2) ? NL[h] : NH[h];
+      f16x2 s, n;
+      if constexpr (T == GQ_Q5_K) {           // elements 8qq .. 8qq+7: codes as bytes
+        const int sh = (qq < 2) ? 0 : 4;
+        const uint32_t W = ws.qh[h] >> (8 * qq);
+        bytes8(kE1024, ((D0 >> sh) & 0x0F0F0F0Fu) | bits_to_b4(W),
+               ((D1 >> sh) & 0x0F0F0F0Fu) | bits_to_b4(W >> 4), v);
+        s = SL[h];
+        n = NL[h];
+      } else {
+        const uint32_t msk = (qq < 2) ? 0x0F0F0F0Fu : 0xF0F0F0F0u;
+        bytes8(kE1024, D0 & msk, D1 & msk, v);
+        s = (qq < 2) ? SL[h] : SH[h];
+        n = (qq < 2) ? NL[h] : NH[h];
+      }
       const f16x8 B = cat8(__builtin_elementwise_fma(v[0], s, n), __builtin_elementwise_fma(v[1], s, n),
                            __builtin_elementwise_fma(v[2], s, n), __builtin_elementwise_fma(v[3], s, n));
 #pragma unroll
@@ -345,6 +397,43 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, c
     for (int mt = 0; mt < MT; mt++) {
       if constexpr (XLO) acc[mt] += (d * iv) * Pk[mt];
       else acc[mt] += d * Pk[mt];
+    }
+  } else if constexpr (T == GQ_Q4_1) {
+    // B = RNE_fp16(w 2^k) per block, w = d q + m formed exactly by the mixed
+    // FMA (k puts the block's bound 15 |d| + |m| in [2^13, 2^14)); the
+    // block's products take 2^-k
+    const u32x4 dq = *reinterpret_cast<const u32x4*>(ww + WSQ41::WD + t * 16);   // 8 fp16 d
+    const u32x4 mq = *reinterpret_cast<const u32x4*>(ww + WSQ41::WQ + t * 16);   // 8 fp16 m
+    const int co = t * 8 * 16 + 8 * (g & 1), sh = 4 * (g >> 1);
+    f32x4v as[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) as[mt] = z;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const u32x2 cc = *reinterpret_cast<const u32x2*>(ww + co + j * 16);
+      const uint32_t c0 = (cc.x >> sh) & 0x0F0F0F0Fu, c1 = (cc.y >> sh) & 0x0F0F0F0Fu;
+      const float d = h2f(dq[j >> 1] >> (16 * (j & 1))), m = h2f(mq[j >> 1] >> (16 * (j & 1)));
+      const int k = pow2_exp_for<14>(fmaf(15.f, fabsf(d), fabsf(m)));
+      const float s24 = __builtin_ldexpf(d, k + 24), nb = __builtin_ldexpf(m, k);
+      const uint32_t e0 = c0 & 0x00FF00FFu, o0 = (c0 >> 8) & 0x00FF00FFu;
+      const uint32_t e1 = c1 & 0x00FF00FFu, o1 = (c1 >> 8) & 0x00FF00FFu;
+      const f16x8 B = __builtin_bit_cast(
+          f16x8, u32x4{mixpair<0>(e0, o0, s24, nb), mixpair<1>(e0, o0, s24, nb),
+                       mixpair<0>(e1, o1, s24, nb), mixpair<1>(e1, o1, s24, nb)});
+      f32x4v Pk[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) Pk[mt] = z;
+      mma<XLO, P>(xw, t, 4 * j + g, B, Pk);
+      const float inv = __builtin_ldexpf(1.f, -k);
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        if constexpr (XLO) as[mt] += inv * Pk[mt];
+        else acc[mt] += inv * Pk[mt];
+      }
+    }
+    if constexpr (XLO) {
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) acc[mt] += iv * as[mt];
     }
   } else {
     using W = WS32<T>;
@@ -413,7 +502,7 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
                                              int rb, const void* __restrict__ xv, int n,
                                              float* __restrict__ y, int tiles, int passes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr bool KQ = (T == GQ_Q4_K || T == GQ_Q6_K);
+  constexpr bool KQ = (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K);
   constexpr int ES = XLO ? 4 : 2;
   constexpr int XB = P * 512 * (XLO ? 2 : 1);   // LDS bytes per wave: activations,
   constexpr int WB = kWB<T>;                    // then staged weights (32-weight types)
@@ -490,7 +579,8 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
       stage_x<XLO, P>(xw, sv, xs[i], lane);
       if constexpr (!KQ) {                    // RT is 1 for these types
         const int b = 8 * (w + (m0 + i) * KS) + 2 * g;
-        stage_w<T>(ww, ws[i][0], r, g, b < nblk, b + 1 < nblk);
+        if constexpr (T == GQ_Q4_1) stage_w_q41(ww, ws[i][0], r, g, b < nblk, b + 1 < nblk);
+        else stage_w<T>(ww, ws[i][0], r, g, b < nblk, b + 1 < nblk);
       }
 #pragma unroll
       for (int rt = 0; rt < RT; rt++)         // slabs past cnt read as zeros
@@ -595,7 +685,7 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // slab, halving the activation reads, which there outweigh the weights'
   // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;
   // with fewer tiles the halved wave count costs more than it saves)
-  if constexpr (T == GQ_Q4_K || T == GQ_Q6_K) {
+  if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K) {
     if ((rows + 15) / 16 >= GQ_MMV_RT2_TILES)
       return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2), st);
   }
@@ -631,6 +721,8 @@ hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, co
     GQ_MMV_CASE(GQ_Q8_0)
     GQ_MMV_CASE(GQ_Q4_K)
     GQ_MMV_CASE(GQ_Q6_K)
+    GQ_MMV_CASE(GQ_Q4_1)
+    GQ_MMV_CASE(GQ_Q5_K)
 #undef GQ_MMV_CASE
   }
   return hipErrorInvalidValue;

@@ -34,18 +34,30 @@ __device__ __forceinline__ void seg_dequant(const uint8_t* row, int s, float w[3
         w[j + 16] = d * (float)(hi - off);
       }
     }
-  } else if constexpr (T == GQ_Q4_K) {
+  } else if constexpr (T == GQ_Q4_1) {
+    const float d = h2f(ld2u(b)), m = h2f(ld2u(b + 2));
+    const uint8_t* qs = b + 4;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      w[j] = fmaf(d, (float)(qs[j] & 15), m);      // d*q exact: one rounding
+      w[j + 16] = fmaf(d, (float)(qs[j] >> 4), m);
+    }
+  } else if constexpr (T == GQ_Q4_K || T == GQ_Q5_K) {
+    constexpr bool Q5 = (T == GQ_Q5_K);
     const int i = s & 7;
     u32x4 h = ld16a(b);
     float d = h2f(h.x), dmin = h2f(h.x >> 16);
     uint32_t p = q4k_pair(h.y, h.z, h.w, i);
     float a = d * (float)(p & 63u);            // exact
     float bm = dmin * (float)(p >> 6);         // exact
-    const uint8_t* qs = b + 16 + 16 * i;
+    const uint8_t* qs = b + (Q5 ? 48 : 16) + 16 * i;
+    const uint32_t qh = Q5 ? ld4u(b + 16 + 4 * i) : 0u;   // fifth bits of the sub-block
 #pragma unroll
     for (int k = 0; k < 16; k++) {
-      float t0 = a * (float)(qs[k] & 15);      // exact
-      float t1 = a * (float)(qs[k] >> 4);
+      const int c0 = (qs[k] & 15) | (int)(((qh >> k) & 1u) << 4);
+      const int c1 = (qs[k] >> 4) | (int)(((qh >> (k + 16)) & 1u) << 4);
+      float t0 = a * (float)c0;                // exact
+      float t1 = a * (float)c1;
       w[k] = t0 - bm;                          // one rounding
       w[k + 16] = t1 - bm;
     }
@@ -120,6 +132,19 @@ __device__ uint32_t d_cover(double maxval, double levels) {
   return h;
 }
 
+// Largest finite fp16 <= v (saturating at -65504), v finite.
+__device__ uint32_t d_half_floor(double v) {
+  if (v >= 0.0) {
+    uint32_t h = d_half_up(v);
+    if (h > 0x7BFFu) return 0x7BFFu;
+    if (d_h2d(h) > v) h--;
+    return h;
+  }
+  uint32_t h = d_half_up(-v);
+  if (h > 0x7BFFu) h = 0x7BFFu;
+  return 0x8000u | h;
+}
+
 __device__ int d_clampi(double v, int lo, int hi) {
   if (v < (double)lo) return lo;
   if (v > (double)hi) return hi;
@@ -150,7 +175,26 @@ __device__ void quant_block(const float* __restrict__ w, uint8_t* out) {
       for (int t = 0; t < 4; t++) out[2 + t] = (uint8_t)(qh >> (8 * t));
       for (int j = 0; j < 16; j++) out[6 + j] = (uint8_t)((q[j] & 15) | ((q[j + 16] & 15) << 4));
     }
-  } else if constexpr (T == GQ_Q4_K) {
+  } else if constexpr (T == GQ_Q4_1) {
+    double lo = INFINITY, hi = -INFINITY;
+    for (int j = 0; j < 32; j++) {
+      lo = fmin(lo, (double)w[j]);
+      hi = fmax(hi, (double)w[j]);
+    }
+    const uint32_t m16 = d_half_floor(lo);
+    const double m = d_h2d(m16);
+    const uint32_t d16 = d_cover(hi - m, 15.0);
+    const double d = d_h2d(d16);
+    int q[32];
+    for (int j = 0; j < 32; j++) q[j] = (d == 0.0) ? 0 : d_clampi(round(((double)w[j] - m) / d), 0, 15);
+    out[0] = (uint8_t)d16;
+    out[1] = (uint8_t)(d16 >> 8);
+    out[2] = (uint8_t)m16;
+    out[3] = (uint8_t)(m16 >> 8);
+    for (int j = 0; j < 16; j++) out[4 + j] = (uint8_t)(q[j] | (q[j + 16] << 4));
+  } else if constexpr (T == GQ_Q4_K || T == GQ_Q5_K) {
+    constexpr int L = (T == GQ_Q5_K) ? 31 : 15;
+    constexpr int QS = (T == GQ_Q5_K) ? 48 : 16;
     double hi[8], Mp[8], sp[8];
     double M[8];
     double maxM = 0.0, maxs = 0.0;
@@ -171,7 +215,7 @@ __device__ void quant_block(const float* __restrict__ w, uint8_t* out) {
     for (int i = 0; i < 8; i++) {
       mn[i] = (dmin == 0.0) ? 0 : d_clampi(ceil(M[i] / dmin), 0, 63);
       Mp[i] = dmin * (double)mn[i];
-      sp[i] = (hi[i] + Mp[i]) / 15.0;
+      sp[i] = (hi[i] + Mp[i]) / (double)L;
       maxs = fmax(maxs, sp[i]);
     }
     uint32_t d16 = d_cover(maxs, 63.0);
@@ -192,12 +236,19 @@ __device__ void quant_block(const float* __restrict__ w, uint8_t* out) {
     }
     for (int t = 0; t < 8; t++) out[4 + t] = (uint8_t)(lo64 >> (8 * t));
     for (int t = 0; t < 4; t++) out[12 + t] = (uint8_t)(hi32 >> (8 * t));
+    if constexpr (T == GQ_Q5_K)
+      for (int t = 0; t < 32; t++) out[16 + t] = 0;
     for (int i = 0; i < 8; i++) {
       double step = d * (double)sc[i];
       for (int k = 0; k < 16; k++) {
-        int q0 = (step == 0.0) ? 0 : d_clampi(round(((double)w[32 * i + k] + Mp[i]) / step), 0, 15);
-        int q1 = (step == 0.0) ? 0 : d_clampi(round(((double)w[32 * i + k + 16] + Mp[i]) / step), 0, 15);
-        out[16 + 16 * i + k] = (uint8_t)(q0 | (q1 << 4));
+        int q0 = (step == 0.0) ? 0 : d_clampi(round(((double)w[32 * i + k] + Mp[i]) / step), 0, L);
+        int q1 = (step == 0.0) ? 0 : d_clampi(round(((double)w[32 * i + k + 16] + Mp[i]) / step), 0, L);
+        out[QS + 16 * i + k] = (uint8_t)((q0 & 15) | ((q1 & 15) << 4));
+        if constexpr (T == GQ_Q5_K) {         // bit e of the fifth-bit plane: element e
+          const int e0 = 32 * i + k, e1 = e0 + 16;
+          out[16 + e0 / 8] |= (uint8_t)(((q0 >> 4) & 1) << (e0 % 8));
+          out[16 + e1 / 8] |= (uint8_t)(((q1 >> 4) & 1) << (e1 % 8));
+        }
       }
     }
   } else {  // GQ_Q6_K
@@ -274,6 +325,8 @@ hipError_t launch_dequant(int type, const void* blob, int64_t rows, int64_t cols
     case GQ_Q8_0: return dequant_t<GQ_Q8_0>(blob, rows, cols, out, f16, st);
     case GQ_Q4_K: return dequant_t<GQ_Q4_K>(blob, rows, cols, out, f16, st);
     case GQ_Q6_K: return dequant_t<GQ_Q6_K>(blob, rows, cols, out, f16, st);
+    case GQ_Q4_1: return dequant_t<GQ_Q4_1>(blob, rows, cols, out, f16, st);
+    case GQ_Q5_K: return dequant_t<GQ_Q5_K>(blob, rows, cols, out, f16, st);
   }
   return hipErrorInvalidValue;
 }
@@ -295,6 +348,8 @@ hipError_t launch_quantize(int type, const float* w, int64_t rows, int64_t cols,
     case GQ_Q8_0: return quantize_t<GQ_Q8_0>(w, rows, cols, blob, st);
     case GQ_Q4_K: return quantize_t<GQ_Q4_K>(w, rows, cols, blob, st);
     case GQ_Q6_K: return quantize_t<GQ_Q6_K>(w, rows, cols, blob, st);
+    case GQ_Q4_1: return quantize_t<GQ_Q4_1>(w, rows, cols, blob, st);
+    case GQ_Q5_K: return quantize_t<GQ_Q5_K>(w, rows, cols, blob, st);
   }
   return hipErrorInvalidValue;
 }

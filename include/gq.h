@@ -49,7 +49,9 @@ enum {
     GQ_Q5_0 = 3,   /* 32 weights, 22 B:  fp16 d, u32 fifth bits, 16 B codes; w = d*(q-16) */
     GQ_Q8_0 = 4,   /* 32 weights, 34 B:  fp16 d, 32 int8 codes; w = d*q */
     GQ_Q4_K = 5,   /* 256 weights, 144 B: fp16 d, fp16 dmin, 12 B 6-bit sc/m, 128 B codes */
-    GQ_Q6_K = 6    /* 256 weights, 210 B: fp16 d, 16 int8 scales, 128 B low, 64 B high bits */
+    GQ_Q6_K = 6,   /* 256 weights, 210 B: fp16 d, 16 int8 scales, 128 B low, 64 B high bits */
+    GQ_Q4_1 = 7,   /* 32 weights, 20 B:  fp16 d, fp16 m, 16 B codes; w = d*q + m */
+    GQ_Q5_K = 8    /* 256 weights, 176 B: Q4_K's fields, 32 B fifth bits, 128 B codes */
 };
 
 /* Error codes. */
@@ -79,6 +81,13 @@ enum {
  *        of 32 owns bytes 16g..16g+15 in Q4_0 nibble order; qh[64] @146, byte
  *        8g+k holds bits 4..5 of elements 32g+k+8u at bits 2u..2u+1 (R).
  *        w = d*(sc*(q-32)).
+ *  Q4_1: d @0; m @2 (signed); qs[16] @4 as Q4_0 (R: "How LLM Inference
+ *        Engines Work", "Loading GGUF Models" names the type only).
+ *        w = d*q + m.
+ *  Q5_K: Q4_K's d, dmin, scales[12] @0..15; qh[32] @16, bit e of the 256-bit
+ *        little-endian field = bit 4 of element e's code; qs[128] @48 as in
+ *        Q4_K (R: 5.5 bpw, "Other k-quants at a glance").  q in 0..31,
+ *        w = (d*sc_i)*q - dmin*m_i.
  *
  * Limits: rows, cols and n_tok below 2^31; rows*RB, n_tok*cols and
  * n_tok*rows below 2^47; cols <= 16384 at n_tok = 1 (x is staged in 64 KB of
@@ -188,9 +197,10 @@ int gq_matmul_decode(const void *weight_blob, const void *up_blob, int ggml_type
 /*
  * Dequantize the whole blob into out[rows][cols] (device, 16-B aligned).
  *   out_type GQ_F32: bit-exact with the stated fp32 operation order: Q4_K
- *     forms a = d*sc and b = dmin*m in fp32 (exact) and rounds once in
- *     a*q - b; Q6_K forms the integer sc*(q-32) and multiplies by d (exact);
- *     the 32-weight types compute d*(q - offset) (exact).
+ *     and Q5_K form a = d*sc and b = dmin*m in fp32 (exact) and round once
+ *     in a*q - b; Q6_K forms the integer sc*(q-32) and multiplies by d
+ *     (exact); Q4_1 rounds once in d*q + m (d*q exact); the other 32-weight
+ *     types compute d*(q - offset) (exact).
  *   out_type GQ_F16: round-to-nearest-even of that fp32 value.
  */
 int gq_dequant(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
@@ -200,7 +210,9 @@ int gq_dequant(const void *weight_blob, int ggml_type, int64_t rows, int64_t col
  * Quantize fp32 w[rows][cols] (device) into a blob (device, rows*RB bytes),
  * all arithmetic in fp64: symmetric absmax blocks for Q4_0 / Q5_0 / Q8_0 and
  * for Q6_K's 16-weight sub-blocks, min/scale sub-blocks for Q4_K ("two-level
- * scaling" and "asymmetric quantization", Hitchhiker's Guide §11.2); stored
+ * scaling" and "asymmetric quantization", Hitchhiker's Guide §11.2; Q5_K
+ * the same with 31 levels, Q4_1 a min rounded down to fp16 and a covering
+ * scale per block); stored
  * fp16 scales are rounded up so every weight is covered, codes are rounded
  * half away from zero.  Weights whose block scale would exceed the largest
  * finite fp16 saturate.  Used to make blobs from fp32 weights on the device.

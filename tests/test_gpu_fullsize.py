@@ -5,7 +5,8 @@ Workloads (shapes as rows x cols, rows = output features):
   * a single Q4_K GEMV at 2048 x 2048 (checked in full);
   * a Llama-7B-shaped decode layer in the Q4_K_M mix at batch 1;
   * a per-type sweep at 4096 x 4096 (Q5_0, Q6_K, Q8_0, 1 % outliers at 10x)
-    plus a 32000 x 4096 Q6_K output head;
+    plus a 32000 x 4096 Q6_K output head, and Q4_1 and Q5_K at 4096 x 4096
+    at 1, 8, 64 and 512 tokens;
   * Q4_K 11008 x 4096 with fp16 activations at 1, 8, 64 and 512 tokens;
   * a Llama-3-8B-shaped layer set at 1, 8 and 64 tokens, with the
     128256 x 4096 Q6_K head.
@@ -73,3 +74,11 @@ def test_q4k_11008_fp16_tokens(n):
 def test_llama3_8b_layer(name, t, rows, cols):
     for n in synth.LLAMA3_8B_TOKENS:
         run_case(t, rows, cols, n, "f32" if n == 1 else "f16", seed=5000 + rows + cols)
+
+
+@pytest.mark.parametrize("t", ["q4_1", "q5_k"])
+def test_new_types_4096(t):
+    """The block types beyond the Q4_K_M recipe at a full 4096 x 4096 size,
+    through the GEMV (fp32 x) and the batched paths (fp16 x)."""
+    for n in synth.GEMM_TOKENS:
+        run_case(t, 4096, 4096, n, "f32" if n == 1 else "f16", seed=6000, outliers=0.01)

@@ -9,15 +9,16 @@ import synth
 import tol_terms
 
 
-def test_q4k_parts_rebuild_the_oracle_dequant(oracle):
+@pytest.mark.parametrize("t", ["q4_k", "q5_k"])
+def test_q4k_parts_rebuild_the_oracle_dequant(oracle, t):
     o = oracle._load()
     rows, cols = 40, 512
-    blob = tol_terms.finite_scales(synth.random_bytes(rows * o.row_bytes("q4_k", cols), seed=81), "q4_k")
-    a, q, b = tol_terms.q4k_parts(blob, rows, cols)
-    assert np.array_equal(a * q - b, o.dequant_f64(blob, "q4_k", rows, cols))
+    blob = tol_terms.finite_scales(synth.random_bytes(rows * o.row_bytes(t, cols), seed=81), t)
+    a, q, b = tol_terms.q4k_parts(blob, rows, cols, t)
+    assert np.array_equal(a * q - b, o.dequant_f64(blob, t, rows, cols))
 
 
-@pytest.mark.parametrize("t", ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k"])
+@pytest.mark.parametrize("t", ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k"])
 def test_row_bound_covers_every_weight(oracle, t):
     o = oracle._load()
     rows, cols = 30, 2 * tol_terms.QK[t]

@@ -8,7 +8,7 @@ activations) every path meets the plain bar
 Two further terms appear on arbitrary bytes, each derived from the arithmetic
 of a path:
 
-  * factored Q4_K sums.  The batch-1 GEMV forms, per 32-weight sub-block,
+  * factored Q4_K and Q5_K sums.  The batch-1 GEMV forms, per 32-weight sub-block,
     a * sum(q x) - b * sum(x) (w = a q - b, Hitchhiker's Guide §11.2), and the
     weight-stream kernel d * P_k - dmin * P_m with P_k = sum((sc q) x) and
     P_m = sum(m x).  Each sum is rounded relative to its own magnitude, so the
@@ -32,8 +32,8 @@ from __future__ import annotations
 
 import numpy as np
 
-QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256}
-BB = {"q4_0": 18, "q5_0": 22, "q8_0": 34, "q4_k": 144, "q6_k": 210}
+QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256}
+BB = {"q4_0": 18, "q5_0": 22, "q8_0": 34, "q4_k": 144, "q6_k": 210, "q4_1": 20, "q5_k": 176}
 EPS_FACTORED = 2.0 ** -16
 EPS_RANGE = 2.0 ** -30
 
@@ -44,18 +44,25 @@ def _f16(b2: np.ndarray) -> np.ndarray:
     return u.view(np.float16).astype(np.float64)
 
 
-def q4k_parts(blob: np.ndarray, rows: int, cols: int):
-    """Per weight (a, q, b) of Q4_K blocks with w = a q - b: a = d sc_i,
-    b = dmin m_i (fp64), q the 4-bit code; arrays of shape [rows, cols]."""
+def q4k_parts(blob: np.ndarray, rows: int, cols: int, t: str = "q4_k"):
+    """Per weight (a, q, b) of Q4_K (or Q5_K) blocks with w = a q - b:
+    a = d sc_i, b = dmin m_i (fp64), q the 4-bit (5-bit) code; arrays of
+    shape [rows, cols].  Q5_K (R15): the fifth-bit plane at bytes 16..47,
+    codes from byte 48."""
     nb = cols // 256
-    blk = blob.reshape(rows, nb, 144)
+    q5 = (t == "q5_k")
+    blk = blob.reshape(rows, nb, BB[t])
     d = _f16(blk[..., 0:2])
     dmin = _f16(blk[..., 2:4])
     bits = np.unpackbits(blk[..., 4:16], axis=-1, bitorder="little")      # 96 bits, LSB first
     fields = (bits.reshape(rows, nb, 16, 6).astype(np.int64) << np.arange(6)).sum(axis=-1)
     sc, mn = fields[..., 0::2], fields[..., 1::2]                          # [rows, nb, 8]
-    qs = blk[..., 16:144].reshape(rows, nb, 8, 16)
+    o = 48 if q5 else 16
+    qs = blk[..., o:o + 128].reshape(rows, nb, 8, 16)
     q = np.concatenate([qs & 15, qs >> 4], axis=-1).astype(np.float64)    # element k, k + 16
+    if q5:
+        hb = np.unpackbits(blk[..., 16:48], axis=-1, bitorder="little")   # bit e: element e
+        q = q + 16.0 * hb.reshape(rows, nb, 8, 32)
     a = (d[..., None] * sc)[..., None] * np.ones(32)
     b = (dmin[..., None] * mn)[..., None] * np.ones(32)
     return a.reshape(rows, cols), q.reshape(rows, cols), b.reshape(rows, cols)
@@ -67,6 +74,10 @@ def row_bound(blob: np.ndarray, t: str, rows: int, cols: int) -> np.ndarray:
     d = np.abs(_f16(blk[..., 0:2]))
     if t == "q4_k":
         u = 945.0 * d + 63.0 * np.abs(_f16(blk[..., 2:4]))
+    elif t == "q5_k":
+        u = 1953.0 * d + 63.0 * np.abs(_f16(blk[..., 2:4]))
+    elif t == "q4_1":
+        u = 15.0 * d + np.abs(_f16(blk[..., 2:4]))
     else:
         u = {"q6_k": 4096.0, "q8_0": 128.0, "q4_0": 8.0, "q5_0": 16.0}[t] * d
     return u.max(axis=1)
@@ -77,8 +88,8 @@ def tolerance(blob, t, rows, cols, x, yabs, w64):
     from the oracle, w64 the oracle's fp64 dequantization [rows, cols]."""
     ax = np.abs(np.asarray(x, dtype=np.float64).reshape(-1, cols))
     tol = 1e-3 * yabs
-    if t == "q4_k":
-        a, q, b = q4k_parts(blob, rows, cols)
+    if t in ("q4_k", "q5_k"):
+        a, q, b = q4k_parts(blob, rows, cols, t)
         tol = tol + EPS_FACTORED * (ax @ (np.abs(a) * q + np.abs(b)).T)
     u = row_bound(blob, t, rows, cols)
     tol = tol + EPS_RANGE * (ax.sum(axis=1)[:, None] * u[None, :]
@@ -91,7 +102,7 @@ def finite_scales(blob: np.ndarray, t: str) -> np.ndarray:
     an all-ones exponent (Inf / NaN) is lowered to 30."""
     out = blob.copy()
     blk = out.reshape(-1, BB[t])
-    for off in ((0, 2) if t == "q4_k" else (0,)):
+    for off in ((0, 2) if t in ("q4_k", "q5_k", "q4_1") else (0,)):
         hi = blk[:, off + 1]
         bad = (hi & 0x7C) == 0x7C
         hi[bad] &= 0xFB                                   # exponent 31 -> 30
