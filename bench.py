@@ -36,7 +36,8 @@ Method:
 Prints one JSON line.  `--profile-launches N` instead runs N plain (ungraphed)
 launches of each layer matrix plus a device copy of known size, and
 `--profile-gemm N` N plain launches of the 512-token GEMM, `--profile-attn N` N
-plain calls of the q8_0 KV-cache attention decode, for rocprofv3
+plain calls of the q8_0 KV-cache attention decode, and `--profile-shape
+TYPE,ROWS,COLS,NTOK,XDT[,N]` N plain launches of any one shape, for rocprofv3
 kernel traces and counters.
 """
 from __future__ import annotations
@@ -88,6 +89,9 @@ def parse():
     p.add_argument("--profile-launches", type=int, default=0)
     p.add_argument("--profile-attn", type=int, default=0, metavar="N",
                    help="only run N plain calls of the q8_0 KV-cache attention decode")
+    p.add_argument("--profile-shape", default="", metavar="TYPE,ROWS,COLS,NTOK,XDT[,N]",
+                   help="only run N (default 50) plain gq_matmul launches of one shape, e.g. "
+                        "q4_k,11008,4096,64,f16 (for rocprofv3 traces and counters)")
     return p.parse_args()
 
 
@@ -552,6 +556,20 @@ def main():
             c.launch(i, sp)
         torch.cuda.synchronize()
         log(f"profile: {args.profile_attn} calls of the q8_0 attention decode")
+        return
+    if args.profile_shape:
+        f = args.profile_shape.split(",")
+        t, rows, cols, n, xdt = f[0], int(f[1]), int(f[2]), int(f[3]), f[4]
+        reps = int(f[5]) if len(f) > 5 else 50
+        m = Mat(f"{t} {rows}x{cols} n={n} {xdt}", t, [("w", rows)], cols, seed=9000, ncopies=1,
+                n_tok=n, x_dtype=xdt)
+        m.ensure_copies(2 * CACHE_BYTES)
+        sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for i in range(reps):
+            m.launch(i, sp)
+        torch.cuda.synchronize()
+        log(f"profile: {reps} launches of {m.name}")
         return
     if args.profile_gemm:
         m = Mat("gemm q4_k 11008x4096 n=512", "q4_k", [("w", 11008)], 4096, seed=9000, ncopies=1,

@@ -51,9 +51,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_EHIP; }
 // rows*cols weights at ~150 (Q6_K ~165, the 32-weight types ~80) TFLOP/s.  The batch goes to the
 // weight-stream kernel, in ceil(n/64) near-equal chunks of at most 64 tokens,
 // when that estimate is lower.
-bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_tok) {
+bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16) {
   const double rate = (type == GQ_Q4_K || type == GQ_Q5_K) ? 150e12 : (type == GQ_Q6_K) ? 165e12 : 80e12;
-  const double gemm_us = gq::gemm_estimate_us(type, rows, cols, n_tok);
+  const double gemm_us = gq::gemm_estimate_us(type, rows, cols, n_tok, x_f16);
   const double pass_us = (double)rows * (double)cols * 32.0 / rate * 1e6;
   const int64_t k = (n_tok + 63) / 64, base = n_tok / k, extra = n_tok % k;
   const int64_t passes = extra * ((base + 16) / 16) + (k - extra) * ((base + 15) / 16);
@@ -134,7 +134,7 @@ int gq_matmul_path(const void* weight_blob, int ggml_type, int64_t rows, int64_t
   const bool xf16 = (x_type == GQ_F16);
   if (n_tok == 1) return hip_status(gq::launch_gemv(ggml_type, weight_blob, rows, cols, x, xf16, y, st));
   if (path == GQ_PATH_AUTO)
-    path = (n_tok <= kStreamOnly || small_batch_chunks_faster(ggml_type, rows, cols, n_tok))
+    path = (n_tok <= kStreamOnly || small_batch_chunks_faster(ggml_type, rows, cols, n_tok, xf16))
                ? GQ_PATH_WEIGHT_STREAM
                : GQ_PATH_TILED;
   if (path == GQ_PATH_TILED)

@@ -40,9 +40,10 @@ hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, co
 // Prefill-sized batches: tiled fp16 GEMM with the weights decoded per tile.
 hipError_t launch_gemm(int type, const void* blob, int64_t rows, int64_t cols, const void* x,
                        bool x_f16, float* y, int64_t n_tok, hipStream_t st);
-// The GEMM's tile shape for rows x n_tok: 0 = 256 rows x 128 tokens (one
-// 8-wave workgroup per CU), 1 = 128 x 128 (4 waves, two per CU), 2 = 128 x 64
-// (4 waves, three per CU); and its estimated time in microseconds.
-int gemm_tile_config(int64_t rows, int64_t n_tok);
-double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok);
+// The GEMM's tile shape (rows x tokens, K groups per tile):
+//   0 = 256 x 128, 1 = 128 x 128, 2 = 128 x 64, 3 = 32 x 64 in 4 K groups,
+//   4 = 64 x 64 in 4 K groups, 5 = 64 x 128 in 2 K groups;
+// and the estimated time of the launch in microseconds.
+int gemm_tile_config(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16);
+double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16);
 }  // namespace gq

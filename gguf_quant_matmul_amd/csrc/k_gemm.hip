@@ -33,6 +33,9 @@
 //   * tiles are mapped so that the token tiles of one weight-row tile run on
 //     one XCD (workgroups go round-robin over the 8 XCDs) and share its L2.
 #include <type_traits>
+#ifdef GQ_TUNE_ENV
+#include <cstdlib>
+#endif
 
 #include "gq_device.h"
 #include "gq_launch.h"
@@ -61,6 +64,21 @@ constexpr int ROWB = BK * 2;                 // bytes of one tile row (64 fp16)
 // bank window (and any 8 rows 8 distinct slots of a 128-byte window).
 __device__ __forceinline__ int swz(int t) { return ((t >> 1) & 7) ^ ((t & 1) << 2); }
 __device__ __forceinline__ int tslot(int t, int c) { return t * 128 + ((c ^ swz(t)) << 4); }
+
+// A copy the compiler cannot fold into its source.  Taking a ring slot's
+// header this way frees the slot's register for the slot's next load; a
+// folded copy keeps the old value in the slot's register until the loop's
+// back edge, where the new load's value is then moved in, and that move
+// waits for the load just issued (draining the whole ring once per
+// super-block).
+__device__ __forceinline__ uint32_t fresh1(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+__device__ __forceinline__ u32x4 fresh(const u32x4& v) {
+  return u32x4{fresh1(v.x), fresh1(v.y), fresh1(v.z), fresh1(v.w)};
+}
 
 __device__ __forceinline__ uint32_t h2pack(float a, float b) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
@@ -292,26 +310,31 @@ template <bool XLO, int NT, int BM> struct AR {
 #define GQ_GEMM_VPM (T == GQ_Q6_K ? 2 : 5)
 #endif
 
-template <int T, bool XLO, int D, int BN, int BM>
-__global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blob, int rows, int cols,
-                                                 int rb, const void* __restrict__ xv, int n,
-                                                 float* __restrict__ y, int tn, int tm) {
-  constexpr int NT = 2 * BN;                 // BN / 32 waves, 32 weight rows each
+// KS > 1 splits the K range of a tile over KS groups of BN / 32 waves: each
+// group walks its own contiguous share of the K steps with its own activation
+// tiles and exponents, and at the end the groups' partial tiles (each taken
+// back to unit scale) are summed in group order through LDS, so the result
+// does not depend on timing.  More waves per tile then hide the step latency
+// where tiles are few (small batches, few weight rows, long rows).
+template <int T, bool XLO, int D, int BN, int BM, int KS = 1>
+__global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict__ blob, int rows, int cols,
+                                                      int rb, const void* __restrict__ xv, int n,
+                                                      float* __restrict__ y, int tn, int tm) {
+  constexpr int NT = 2 * BN;                 // per group: BN / 32 waves, 32 weight rows each
   constexpr int MI = BM / 32;                // 32-token A fragments per 16 columns
   constexpr int NA = XLO ? 2 : 1;            // activation planes: hi (and lo)
   constexpr int ATILE = BM * ROWB;
   static_assert(D % 2 == 0, "even ring depth: LDS buffer parity is static");
-  __shared__ __attribute__((aligned(16))) uint8_t As[2 * NA * ATILE];
+  static_assert(KS == 1 || BN * 4 <= NA * 256, "the partial tiles fit the activation buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t As[KS * 2 * NA * ATILE];
   constexpr int ES = XLO ? 4 : 2;
   constexpr int NL = AR<XLO, NT, BM>::N;     // activation loads per thread per step
   constexpr int NW = NT / 64;
+  constexpr int XKG = (3 * BM + 2 * NW + 3) / 4 * 4;   // per group (16-byte aligned):
   // fp32 x: per token the exponent change of each staged step (double-
   // buffered like the tile), the current exponent, and per wave whether any
   // token of its share changed in the step
-  __shared__ __attribute__((aligned(16))) int xk[XLO ? 3 * BM + 2 * NW : 4];
-  int* const dtok = xk;                      // [2][BM]
-  int* const ktok = xk + 2 * BM;             // [BM]
-  int* const xflag = xk + 3 * BM;            // [2][NW]
+  __shared__ __attribute__((aligned(16))) int xk[XLO ? KS * XKG : 4];
 
   // tile q of XCD x covers tiles x * per .. ; token tiles of a row tile adjacent
   const int total = tn * tm, per = (total + 7) >> 3;
@@ -319,13 +342,22 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
   if (q >= total) return;                    // whole workgroup: uniform
   const int n0 = (q / tm) * BN, m0 = (q % tm) * BM;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kg = (KS > 1) ? (int)threadIdx.x / NT : 0;   // K group
+  const int tid = (int)threadIdx.x - kg * NT, lane = tid & 63, w = tid >> 6;
+  uint8_t* const Ag = As + kg * 2 * NA * ATILE;          // the group's activation tiles
+  int* const dtok = xk + kg * XKG;           // [2][BM]
+  int* const ktok = dtok + 2 * BM;           // [BM]
+  int* const xflag = dtok + 3 * BM;          // [2][NW]
   const int nr = min(BN, rows - n0), nt = min(BM, n - m0);
   const __amdgpu_buffer_rsrc_t WR = make_rsrc(blob + (int64_t)n0 * rb, (uint32_t)(nr * rb));
   const __amdgpu_buffer_rsrc_t XR =
       make_rsrc((const uint8_t*)xv + (int64_t)m0 * cols * ES, (uint32_t)(nt * cols * ES));
   const int nk = (cols + BK - 1) / BK;
   const int nseg = cols >> 5;
+  // the group's K steps: [kbase, kbase + nkg), nkg a multiple of 4 so that a
+  // super-block's steps stay in one group and in ring slots 0..3
+  const int nkg = (KS > 1) ? ((nk + KS - 1) / KS + 3) / 4 * 4 : nk;
+  const int kbase = kg * nkg, kend = min(nk, kbase + nkg);
   // B fragment lane: weight row 32 w + fr of the tile; k half fk = the
   // 32-column segment 2 * step + fk of the row (its chunk ks feeds MFMA ks)
   const int fr = lane & 31, fk = lane >> 5;
@@ -349,12 +381,17 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
   // With a 4-deep ring, ring slot u always holds steps = u mod 4, so only
   // slot 0 (the first step of each super-block) loads the Q4_K header.
   constexpr bool SHARE = BR<T>::kHeader && D == 4;
+  // s: the group's step (global step kbase + s); steps past the group's
+  // range (or the row) read zeros
   auto load = [&](AR<XLO, NT, BM>& a, BR<T>& b, int s, auto hdr) {
-    const int sg = 2 * s + fk;
-    b.template load<decltype(hdr)::value>(WR, vrow, sg, sg < nseg);
-    const int col = s * BK + xc;
+    const int gs = kbase + s;
+    const bool in = gs < kend;
+    const int sg = 2 * gs + fk;
+    b.template load<decltype(hdr)::value>(WR, vrow, sg, in && sg < nseg);
+    const int col = gs * BK + xc;
 #pragma unroll
-    for (int i = 0; i < NL; i++) a.v[i] = bld16(XR, col < cols ? xo[i] + s * BK * ES : kOobOff, 0);
+    for (int i = 0; i < NL; i++)
+      a.v[i] = bld16(XR, (in && col < cols) ? xo[i] + gs * BK * ES : kOobOff, 0);
   };
   // fp32 x: thread slot i always stages the same token, 16 threads per token
   // and step; kx[i] is that token's exponent k (x enters as hi + lo of
@@ -365,7 +402,7 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
 #pragma unroll
   for (int i = 0; i < (XLO ? NL : 1); i++) kx[i] = KNONE;
   auto stage_a = [&](const AR<XLO, NT, BM>& a, int buf) {
-    uint8_t* const A0 = As + buf * NA * ATILE;
+    uint8_t* const A0 = Ag + buf * NA * ATILE;
     bool chg = false;
 #pragma unroll
     for (int i = 0; i < NL; i++) {
@@ -422,7 +459,7 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
     if constexpr (SHARE) {
       // the header, and so U, changes only on a super-block's first step
       if constexpr (decltype(u)::value == 0) {
-        hcur = b.hd;
+        hcur = fresh(b.hd);
         U = BR<T>::bound(hcur);
       }
     } else {
@@ -436,8 +473,8 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
       else if (e + kr > 14) { dpend += 10 - e - kr; kr = 10 - e; }
     }
     const int k = (kr == KNONE) ? 0 : kr;
-    if constexpr (SHARE) b.decode(2 * s + fk, hcur, k, out);
-    else b.decode(2 * s + fk, k, out);
+    if constexpr (SHARE) b.decode(2 * (kbase + s) + fk, hcur, k, out);
+    else b.decode(2 * (kbase + s) + fk, k, out);
   };
   // Before step i's products: bring the accumulators to step i's exponents
   // (row: decided when step i was decoded; fp32 x: when it was staged).
@@ -478,12 +515,12 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
 
   // Steps past the last read zeros (masked loads), so every unrolled step
   // runs unguarded and adds exactly nothing.
-  for (int i0 = 0; i0 < nk; i0 += D) {
+  for (int i0 = 0; i0 < nkg; i0 += D) {
     static_for<D>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
       const int i = i0 + u;
       constexpr int buf = u & 1;             // i0 is a multiple of D, D even
-      const uint8_t* const A0 = As + buf * NA * ATILE;
+      const uint8_t* const A0 = Ag + buf * NA * ATILE;
       constexpr int sl = (u + 1) % D;        // ring slot of step i + 1
       const std::integral_constant<int, sl> slc{};
       rescale(buf);
@@ -536,20 +573,49 @@ __global__ void __launch_bounds__(2 * BN) k_gemm(const uint8_t* __restrict__ blo
   // no exponent, so the accumulators are at (kr, ktok) here; y takes 2^-k.
   const int r = 32 * w + fr;
   const int kw = (kr == KNONE) ? 0 : kr;
+  if constexpr (KS == 1) {
 #pragma unroll
-  for (int mi = 0; mi < MI; mi++)
+    for (int mi = 0; mi < MI; mi++)
 #pragma unroll
-    for (int v = 0; v < 16; v++) {
-      const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
-      int k = kw;
-      if constexpr (XLO) k += (ktok[t] == KNONE) ? 0 : ktok[t];
-      if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = __builtin_ldexpf(acc[mi][v], -k);
+      for (int v = 0; v < 16; v++) {
+        const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
+        int k = kw;
+        if constexpr (XLO) k += (ktok[t] == KNONE) ? 0 : ktok[t];
+        if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = __builtin_ldexpf(acc[mi][v], -k);
+      }
+  } else {
+    // each group's partial tile at unit scale into LDS (over the activation
+    // tiles, which every wave is done with after the loop's last barrier),
+    // then group 0 sums the KS partials in group order
+    float* const red = reinterpret_cast<float*>(As);   // [KS][BN/32][16 MI][64]
+#pragma unroll
+    for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+      for (int v = 0; v < 16; v++) {
+        const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
+        int k = kw;
+        if constexpr (XLO) k += (ktok[t] == KNONE) ? 0 : ktok[t];
+        red[((kg * (BN / 32) + w) * 16 * MI + 16 * mi + v) * 64 + lane] = __builtin_ldexpf(acc[mi][v], -k);
+      }
+    __syncthreads();
+    if (kg == 0) {
+#pragma unroll
+      for (int mi = 0; mi < MI; mi++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) {
+          const int t = mi * 32 + 8 * (v >> 2) + 4 * fk + (v & 3);
+          float sum = 0.f;
+#pragma unroll
+          for (int g = 0; g < KS; g++) sum += red[((g * (BN / 32) + w) * 16 * MI + 16 * mi + v) * 64 + lane];
+          if (t < nt && r < nr) y[(int64_t)(m0 + t) * rows + n0 + r] = sum;
+        }
     }
+  }
 }
 
 namespace {
 
-template <int T, bool XLO, int BN, int BM>
+template <int T, bool XLO, int BN, int BM, int KS = 1, int D = (XLO ? 2 : 4)>
 hipError_t gemm_cfg(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
                     hipStream_t st) {
   const int64_t rb = cols / Geo<T>::QK * Geo<T>::BB;
@@ -558,7 +624,7 @@ hipError_t gemm_cfg(const void* blob, int64_t rows, int64_t cols, const void* x,
   const int64_t tn = (rows + BN - 1) / BN, tm = (n + BM - 1) / BM;
   if (tn * tm >= ((int64_t)1 << 31) / 8) return hipErrorInvalidValue;
   const int64_t grid = (tn * tm + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm<T, XLO, XLO ? 2 : 4, BN, BM>), dim3((unsigned)grid), dim3(2 * BN), 0, st,
+  hipLaunchKernelGGL((k_gemm<T, XLO, D, BN, BM, KS>), dim3((unsigned)grid), dim3(2 * BN * KS), 0, st,
                      (const uint8_t*)blob, (int)rows, (int)cols, (int)rb, x, (int)n, y, (int)tn,
                      (int)tm);
   return hipGetLastError();
@@ -567,42 +633,77 @@ hipError_t gemm_cfg(const void* blob, int64_t rows, int64_t cols, const void* x,
 template <int T, bool XLO>
 hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, int64_t n, float* y,
                   hipStream_t st) {
-  switch (gemm_tile_config(rows, n)) {
-    case 1: return gemm_cfg<T, XLO, 128, 128>(blob, rows, cols, x, n, y, st);
-    case 2: return gemm_cfg<T, XLO, 128, 64>(blob, rows, cols, x, n, y, st);
-    default: return gemm_cfg<T, XLO, 256, 128>(blob, rows, cols, x, n, y, st);
+  const int c = gemm_tile_config(T, rows, cols, n, !XLO);
+  if constexpr (!XLO) {
+    // split K: one-wave groups stage 8 loads per step each, so their ring is
+    // 2 deep (4 would cost a wave per SIMD)
+    if (c == 3) return gemm_cfg<T, false, 32, 64, 4, 2>(blob, rows, cols, x, n, y, st);
+    if (c == 4) return gemm_cfg<T, false, 64, 64, 4, 4>(blob, rows, cols, x, n, y, st);
+    if (c == 5) return gemm_cfg<T, false, 64, 128, 2, 2>(blob, rows, cols, x, n, y, st);
   }
+  if (c == 1) return gemm_cfg<T, XLO, 128, 128>(blob, rows, cols, x, n, y, st);
+  if (c == 2) return gemm_cfg<T, XLO, 128, 64>(blob, rows, cols, x, n, y, st);
+  return gemm_cfg<T, XLO, 256, 128>(blob, rows, cols, x, n, y, st);
 }
 
 }  // namespace
 
-// Every tile walks its whole K range, so a shape with few tiles leaves CUs
-// idle: 256 x 128 tiles when they cover 128 to 256 CUs once; smaller tiles
-// (more workgroups resident per CU, less reuse per decoded weight) when they
-// would cover fewer CUs or the batch fits 64 tokens (128 x 64) or when they
-// need a second round (128 x 128).  Measured (fp16 x): Q4_K 4096 x 4096 at
-// 512 tokens 59 -> 36 us (128 x 64), Q6_K 4096 x 11008 at 512 tokens 300 ->
-// 144 us, Q4_K 22016 x 4096 133 -> 122 us (128 x 128), while 11008 / 12288 /
-// 14336 x 4096 stay fastest on 256 x 128.
-int gemm_tile_config(int64_t rows, int64_t n_tok) {
+// Every tile walks its K range, so a shape with few tiles leaves CUs idle.
+// fp16 x, measured on MI355X (us):
+//   * up to 64 tokens, K split over 4 groups of a workgroup: 64-row tiles
+//     once the rows fill 256 CUs with 32-row tiles (Q4_K 11008 x 4096 at 64
+//     tokens 34.0 -> 25.9, 14336 x 4096 34.3 -> 26.5), 32-row tiles below
+//     that (8192 x 4096 23.0, Q6_K 4096 x 11008 162 -> 72);
+//   * more tokens: 256 x 128 tiles when they cover 128 to 256 CUs once,
+//     128 x 128 past that, 128 x 64 below (Q4_K 4096 x 4096 at 512 tokens
+//     62 -> 37); 32-row split-K tiles when even 128 x 64 tiles are fewer than
+//     128 (Q4_K 1024 x 4096 at 512 37 -> 22); Q6_K, whose decode is the
+//     longest, in 64 x 128 tiles of 2 K groups (4096 x 14336 at 512 185 -> 168).
+// fp32 x keeps one K group per tile (its split variants need more registers
+// than a wave has and are not built).
+int gemm_tile_config(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16) {
+  (void)cols;
+#ifdef GQ_TUNE_ENV
+  if (const char* e = getenv("GQ_GEMM_CFG")) {
+    const int c = atoi(e);
+    if (x_f16 || c < 3) return c;
+  }
+#endif
+  const int64_t t128x64 = (rows + 127) / 128 * ((n_tok + 63) / 64);
+  if (x_f16) {
+    if (n_tok <= 64) return (rows + 31) / 32 > 256 ? 4 : 3;
+    if (t128x64 < 128) return 3;
+    if (type == GQ_Q6_K && t128x64 <= 256) return 5;
+  }
   if (n_tok <= 64) return 2;
   const int64_t big = (rows + 255) / 256 * ((n_tok + 127) / 128);
   if (big > 256) return 1;
   return big >= 128 ? 0 : 2;
 }
 
-// Rounds of resident tiles x K steps x the measured time of a step at that
-// tile shape, for Q4_K, Q6_K, Q8_0 / Q5_0 and Q4_0.
-double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok) {
-  static const double step_us[3][4] = {
-      {1.05, 1.75, 1.4, 1.2}, {0.9, 1.3, 1.2, 1.0}, {0.57, 0.95, 0.7, 0.5}};
-  static const int64_t bn[3] = {256, 128, 128}, bm[3] = {128, 128, 64}, slots[3] = {256, 512, 768};
-  const int c = gemm_tile_config(rows, n_tok);
-  const int tc = (type == GQ_Q4_K) ? 0 : (type == GQ_Q6_K || type == GQ_Q5_K) ? 1
+// A launch's time: a fixed start (first loads in flight, tail) plus the K
+// steps of a tile times the measured time of one step at that tile shape,
+// stretched by the tiles past one per CU.
+double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16) {
+  // per tile shape: rows, tokens, K groups, and a step's time per type
+  // (Q4_K / Q5_K, Q6_K, Q8_0 / Q5_0 / Q4_1, Q4_0)
+  struct Cfg {
+    int64_t bn, bm, ks;
+    double step_us[4];
+  };
+  static const Cfg cfg[6] = {
+      {256, 128, 1, {1.13, 1.75, 1.4, 1.2}}, {128, 128, 1, {0.9, 1.3, 1.2, 1.0}},
+      {128, 64, 1, {0.5, 0.82, 0.81, 0.6}},  {32, 64, 4, {1.2, 1.6, 1.6, 1.3}},
+      {64, 64, 4, {1.4, 2.3, 2.2, 1.75}},    {64, 128, 2, {1.22, 1.5, 1.7, 1.3}}};
+  int c = gemm_tile_config(type, rows, cols, n_tok, x_f16);
+  if (c < 0 || c > 5) c = 0;
+  const Cfg& f = cfg[c];
+  const int tc = (type == GQ_Q4_K || type == GQ_Q5_K) ? 0 : (type == GQ_Q6_K) ? 1
                  : (type == GQ_Q4_0) ? 3 : 2;
-  const int64_t tiles = (rows + bn[c] - 1) / bn[c] * ((n_tok + bm[c] - 1) / bm[c]);
-  return (double)((tiles + slots[c] - 1) / slots[c]) * (double)((cols + BK - 1) / BK) *
-         step_us[c][tc];
+  const double tiles = (double)((rows + f.bn - 1) / f.bn * ((n_tok + f.bm - 1) / f.bm));
+  const double steps = (double)(((cols + BK - 1) / BK + f.ks - 1) / f.ks);
+  const double load = tiles > 256.0 ? tiles / 256.0 : 1.0;
+  return 4.0 + load * steps * f.step_us[tc];
 }
 
 hipError_t launch_gemm(int type, const void* blob, int64_t rows, int64_t cols, const void* x,

@@ -271,13 +271,18 @@ def test_gemm_partial_wave_full_size(t, rows, cols, n):
 @pytest.mark.parametrize("t,rows,cols,n,xdt", [
     ("q4_k", 32768, 256, 100, "f16"),    # 128 tiles of 256 x 128: the large tile shape, ragged tokens
     ("q8_0", 8400, 512, 1030, "f32"),    # 297 large tiles -> 128 x 128 tiles, ragged rows and tokens
-    ("q6_k", 1000, 768, 77, "f16"),      # few tiles -> 128 x 64 tiles, ragged rows and tokens
+    ("q6_k", 1000, 768, 77, "f16"),      # few tiles -> 32-row tiles in 4 K groups, ragged
     ("q4_0", 4096, 4096, 512, "f16"),    # 64 large tiles -> 256 tiles of 128 x 64
+    ("q6_k", 1000, 768, 40, "f32"),      # fp32 x up to 64 tokens: 128 x 64 tiles
+    ("q5_k", 8200, 512, 40, "f16"),      # > 256 32-row tiles: 64-row tiles in 4 K groups, ragged
+    ("q4_1", 9000, 768, 64, "f16"),      # 64 x 64 in 4 K groups, the last group past the end of K
+    ("q6_k", 2000, 768, 460, "f16"),     # Q6_K, 128 tiles of 128 x 64 -> 64 x 128 in 2 K groups
 ])
 def test_gemm_tile_shapes(t, rows, cols, n, xdt):
     """Each tile shape of the tiled GEMM (chosen by how many CUs the tiles
-    cover) with ragged edges: sampled rows (all tokens) against the oracle,
-    and two calls bit-identical."""
+    cover, and for up to 64 tokens or few tiles with K split over groups of
+    one workgroup) with ragged edges: sampled rows (all tokens) against the
+    oracle, and two calls bit-identical."""
     _, blob = quantized(t, rows, cols, seed=97)
     bd = to_dev(blob)
     say(f"gemm tile shape {t} {rows}x{cols} n={n} x={xdt}")
