@@ -26,6 +26,16 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled,
+// so that register arrays indexed by the constant stay in registers.
+template <int N, int I = 0, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 __device__ __forceinline__ u32x4 ld16u(const uint8_t* p) {
   u32x4u v = *reinterpret_cast<const u32x4u*>(p);
   return u32x4{v.x, v.y, v.z, v.w};

@@ -46,15 +46,6 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>), unrolled.
-template <int N, int I = 0, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<N, I + 1>(f);
-  }
-}
-
 constexpr int BK = 64;
 constexpr int KNONE = 1 << 20;               // no nonzero block / activation seen yet
 constexpr int ROWB = BK * 2;                 // bytes of one tile row (64 fp16)
@@ -383,7 +374,7 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
   constexpr bool SHARE = BR<T>::kHeader && D == 4;
   // s: the group's step (global step kbase + s); steps past the group's
   // range (or the row) read zeros
-  auto load = [&](AR<XLO, NT, BM>& a, BR<T>& b, int s, auto hdr) {
+  auto load = [&](AR<XLO, NT, BM>& a, BR<T>& b, int s, auto hdr) __attribute__((always_inline)) {
     const int gs = kbase + s;
     const bool in = gs < kend;
     const int sg = 2 * gs + fk;
@@ -401,7 +392,7 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
   int kx[XLO ? NL : 1];
 #pragma unroll
   for (int i = 0; i < (XLO ? NL : 1); i++) kx[i] = KNONE;
-  auto stage_a = [&](const AR<XLO, NT, BM>& a, int buf) {
+  auto stage_a = [&](const AR<XLO, NT, BM>& a, int buf) __attribute__((always_inline)) {
     uint8_t* const A0 = Ag + buf * NA * ATILE;
     bool chg = false;
 #pragma unroll
@@ -454,7 +445,7 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
   // (dpend holds the change until then).  fp16 then carries every weight
   // within 2^-24 of its row's largest bound to 11 bits.
   int kr = KNONE, dpend = 0;
-  auto decode = [&](BR<T>& b, int s, u32x4 out[4], auto u) {
+  auto decode = [&](BR<T>& b, int s, u32x4 out[4], auto u) __attribute__((always_inline)) {
     float U = 0.f;                           // 0: no change
     if constexpr (SHARE) {
       // the header, and so U, changes only on a super-block's first step
@@ -479,7 +470,7 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
   // Before step i's products: bring the accumulators to step i's exponents
   // (row: decided when step i was decoded; fp32 x: when it was staged).
   // Both only ever fall, so this is a rare, uniform branch.
-  auto rescale = [&](int buf) {
+  auto rescale = [&](int buf) __attribute__((always_inline)) {
     bool any = __builtin_amdgcn_ballot_w64(dpend != 0) != 0;
     if constexpr (XLO) {
       int fl = 0;
@@ -529,7 +520,7 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
       decode(rw[sl], i + 1, bq[buf ^ 1], slc);
       // A fragments of sub-step ks + 1 are read while sub-step ks multiplies
       f16x8 af[2][NA][MI];
-      auto read_a = [&](int ks, f16x8 (&f)[NA][MI]) {
+      auto read_a = [&](int ks, f16x8 (&f)[NA][MI]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mi = 0; mi < MI; mi++)
 #pragma unroll
