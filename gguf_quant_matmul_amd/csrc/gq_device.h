@@ -301,6 +301,20 @@ __device__ __forceinline__ float row16_max(float v) {
   return fmaxf(v, dpp(v, std::integral_constant<int, 0xB1>{})); // quad_perm [1,0,3,2]
 }
 
+// Sum over each 16-lane row, in every lane of the row (the lanes may differ
+// in the rounding order of the additions; callers keep one lane's result).
+__device__ __forceinline__ float row16_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                                 decltype(ctrl)::value, 0xF, 0xF,
+                                                                 false));
+  };
+  v += dpp(v, std::integral_constant<int, 0x128>{});   // row_ror:8
+  v += dpp(v, std::integral_constant<int, 0x124>{});   // row_ror:4
+  v += dpp(v, std::integral_constant<int, 0x4E>{});    // quad_perm [2,3,0,1]
+  return v + dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+}
+
 // Per-column max over all 64 lanes of N columns m[0..N-1] (N = 8 or 16,
 // values >= 0), transposed so that few instructions serve all columns:
 // v_permlane32_swap halves the lane count per column while pairing column t

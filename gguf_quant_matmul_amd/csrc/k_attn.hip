@@ -28,6 +28,9 @@ constexpr int ATT_LDS = 65536;            // LDS budget of the part kernel
 #ifndef GQ_ATT_COMBINE_UNROLL
 #define GQ_ATT_COMBINE_UNROLL 8           // chunks per thread in flight in the combine
 #endif
+#ifndef GQ_ATT_WGS
+#define GQ_ATT_WGS 1024                   // part-kernel workgroups per call
+#endif
 #ifndef GQ_ATT_WAVES
 #define GQ_ATT_WAVES 4
 #endif
@@ -177,11 +180,19 @@ k_attn_part(const uint8_t* __restrict__ kc,
   const int n_heads = n_kv * n_rep;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc, cache_bytes), rv = make_rsrc(vc, cache_bytes);
 
-  // Every load of the chunk goes out first, so the workgroup waits one
-  // memory latency: the V blocks (one block per thread and round; blocks
-  // past the chunk's end read as zero) and the K fragments of the scores.
+  // Every load of the chunk goes out first (loads complete in issue order):
+  // the query rows, then the V blocks and the K fragments of the scores.
+  constexpr int QPT = (NRP * HD + 255) / 256;        // query values per thread, at most
+  float qreg[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; i++) {
+    const int idx = tid + 256 * i;
+    qreg[i] = (idx < n_rep * HD) ? q[g * n_rep * HD + idx] : 0.f;
+  }
   constexpr int CAP = ATT_CHUNK_CAP(NB);
   constexpr int TILES = CAP / 64;                    // 16-position tiles per wave
+  // the V blocks: one block per thread and round; blocks past the chunk's
+  // end read as zero
   constexpr int VIT = CAP * NB / 256;
   typename KB::Raw vr[VIT];
 #pragma unroll
@@ -205,7 +216,12 @@ k_attn_part(const uint8_t* __restrict__ kc,
 #pragma unroll
     for (int bb = 0; bb < NB; bb++) kw[s][bb] = bld12(rk, o + bb * BB, KB::win_off(kg));
   }
-  for (int i = tid; i < n_rep * HD; i += 256) qs[i] = q[g * n_rep * HD + i];
+#pragma unroll
+  for (int i = 0; i < QPT; i++) {
+    const int idx = tid + 256 * i;
+    if (idx < n_rep * HD) qs[idx] = qreg[i];
+  }
+  // the V blocks into LDS (the loads have been in flight since the start)
 #pragma unroll
   for (int it = 0; it < VIT; it++) {
     const int qb = tid + 256 * it, lp = qb / NB, bb = qb % NB;
@@ -279,28 +295,36 @@ k_attn_part(const uint8_t* __restrict__ kc,
   }
   __syncthreads();
 
-  // the chunk's softmax statistics, one wave per query head; padded heads
-  // get zero weights
-  for (int r = wave; r < NRP; r += 4) {
-    float* const sr = sc + r * chunk;
-    if (r >= n_rep) {
-      for (int i = lane; i < chunk; i += 64) sr[i] = 0.f;
-      continue;
-    }
-    float m = -INFINITY;
-    for (int i = lane; i < chunk; i += 64) m = fmaxf(m, sr[i]);
+  // the chunk's softmax statistics, 16 lanes per query head (lane l of wave
+  // w: head 4w + l / 16, positions 4(l % 16) + 64 i), reduced on the DPP
+  // network; padded heads get zero weights
+  {
+    const int hr = 4 * wave + (lane >> 4), hp = 4 * (lane & 15);
+    if (hr < NRP) {
+      float* const sr = sc + hr * chunk;
+      if (hr >= n_rep) {
+        for (int i = hp; i < chunk; i += 64) *reinterpret_cast<f32x4*>(sr + i) = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        float m = -INFINITY;
+        for (int i = hp; i < chunk; i += 64) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sr + i);
+          m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        }
+        m = row16_max(m);
+        float l = 0.f;
+        for (int i = hp; i < chunk; i += 64) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(sr + i);
 #pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
-    float l = 0.f;
-    for (int i = lane; i < chunk; i += 64) {
-      const float p = expf(sr[i] - m);
-      sr[i] = p;
-      l += p;
-    }
-    l = wave_sum(l);
-    if (lane == 0) {
-      st[2 * r] = m;
-      st[2 * r + 1] = l;
+          for (int e = 0; e < 4; e++) v[e] = expf(v[e] - m);
+          *reinterpret_cast<f32x4*>(sr + i) = v;
+          l += (v.x + v.y) + (v.z + v.w);
+        }
+        l = row16_sum(l);
+        if ((lane & 15) == 0) {
+          st[2 * hr] = m;
+          st[2 * hr + 1] = l;
+        }
+      }
     }
   }
   __syncthreads();
@@ -424,7 +448,7 @@ AttnPlan attn_plan(int64_t kv_len, int n_kv, int n_rep, int head_dim) {
          attn_lds(n_rep, attn_nrp(n_rep), chunk_max, nb, nb * KvBlock<GQ_Q8_0>::CODE_BYTES).bytes >
              ATT_LDS)
     chunk_max -= 64;
-  const int64_t target = (1024 + n_kv - 1) / n_kv;
+  const int64_t target = (GQ_ATT_WGS + n_kv - 1) / n_kv;
   int64_t chunk = (kv_len + target - 1) / target;
   chunk = (chunk + 63) / 64 * 64;
   if (chunk < 64) chunk = 64;
