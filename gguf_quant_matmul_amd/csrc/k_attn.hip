@@ -26,7 +26,7 @@ namespace gq {
 constexpr int ATT_MAX_REP = 16;           // query heads per KV head
 constexpr int ATT_LDS = 65536;            // LDS budget of the part kernel
 #ifndef GQ_ATT_COMBINE_UNROLL
-#define GQ_ATT_COMBINE_UNROLL 8           // chunks per thread in flight in the combine
+#define GQ_ATT_COMBINE_UNROLL 16          // chunks per thread and round in the combine
 #endif
 #ifndef GQ_ATT_WGS
 #define GQ_ATT_WGS 1024                   // part-kernel workgroups per call
@@ -397,44 +397,62 @@ k_attn_part(const uint8_t* __restrict__ kc,
 }
 
 // out[h][d] from the per-chunk statistics, in a fixed order.  Workgroup
-// (h, column slice of 32): the largest chunk max M (thread-strided maxima,
-// then a cross-lane and a cross-wave max), then, for its 32 columns, the sums over chunks of
-// e^(m_c - M) acc_c and e^(m_c - M) l_c, each of the 8 threads of a column
-// taking every 8th chunk (their loads independent of one another), the 8
-// partial sums added in slice order.
+// (h, column slice of 32): thread (d, sl) takes chunks sl, sl + 8, ...,
+// GQ_ATT_COMBINE_UNROLL of them per round with all their loads in flight,
+// and keeps a running max m and, at that max, num = sum e^(m_c - m) acc_c[d]
+// and den = sum e^(m_c - m) l_c; the 8 slices are then merged in slice order
+// at their largest m.
 __global__ void __launch_bounds__(256) k_attn_combine(const float* __restrict__ part,
                                                       int n_chunks, int n_heads, int hd,
                                                       float* __restrict__ out) {
-  __shared__ float red[256], rden[256];
+  constexpr int U = GQ_ATT_COMBINE_UNROLL;
+  __shared__ float rm[256], rnum[256], rden[256];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int64_t stride = (int64_t)n_heads * (hd + 2);
   const float* const p0 = part + (int64_t)h * (hd + 2);
-  float mx = -INFINITY;
-  for (int c = tid; c < n_chunks; c += 256) mx = fmaxf(mx, p0[c * stride + hd]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m, 64));   // max is exact
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
   const int d = 32 * blockIdx.y + (tid & 31), sl = tid >> 5;
-  float num = 0.f, den = 0.f;
-#pragma unroll GQ_ATT_COMBINE_UNROLL
-  for (int c = sl; c < n_chunks; c += 8) {
-    const float* const p = p0 + c * stride;
-    const float w = expf(p[hd] - mx);
-    num = fmaf(w, p[d], num);
-    den = fmaf(w, p[hd + 1], den);
+  float m = -INFINITY, num = 0.f, den = 0.f;
+  for (int c0 = sl; c0 < n_chunks; c0 += 8 * U) {
+    float mc[U], ac[U], lc[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int c = c0 + 8 * u;
+      const float* const p = p0 + (int64_t)min(c, n_chunks - 1) * stride;   // past the last: weight 0
+      mc[u] = (c < n_chunks) ? p[hd] : -INFINITY;
+      ac[u] = p[d];
+      lc[u] = p[hd + 1];
+    }
+    float mx = m;
+#pragma unroll
+    for (int u = 0; u < U; u++) mx = fmaxf(mx, mc[u]);
+    if (mx > -INFINITY) {
+      const float r = expf(m - mx);            // 0 while nothing is summed (m = -inf)
+      num *= r;
+      den *= r;
+#pragma unroll
+      for (int u = 0; u < U; u++) {
+        const float w = expf(mc[u] - mx);
+        num = fmaf(w, ac[u], num);
+        den = fmaf(w, lc[u], den);
+      }
+      m = mx;
+    }
   }
-  red[tid] = num;
+  rm[tid] = m;
+  rnum[tid] = num;
   rden[tid] = den;
   __syncthreads();
   if (sl == 0) {
-    for (int k = 1; k < 8; k++) {
-      num += red[32 * k + (tid & 31)];
-      den += rden[32 * k + (tid & 31)];
+    float M = m;
+    for (int k = 1; k < 8; k++) M = fmaxf(M, rm[32 * k + (tid & 31)]);
+    float nn = 0.f, dd = 0.f;
+    for (int k = 0; k < 8; k++) {
+      const float mk = rm[32 * k + (tid & 31)];
+      const float w = (mk == -INFINITY) ? 0.f : expf(mk - M);
+      nn = fmaf(w, rnum[32 * k + (tid & 31)], nn);
+      dd = fmaf(w, rden[32 * k + (tid & 31)], dd);
     }
-    out[(int64_t)h * hd + d] = num / den;
+    out[(int64_t)h * hd + d] = nn / dd;
   }
 }
 
