@@ -644,7 +644,9 @@ hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, i
 //   * up to 64 tokens, K split over 4 groups of a workgroup: 64-row tiles
 //     once the rows fill 256 CUs with 32-row tiles (Q4_K 11008 x 4096 at 64
 //     tokens 34.0 -> 25.9, 14336 x 4096 34.3 -> 26.5), 32-row tiles below
-//     that (8192 x 4096 23.0, Q6_K 4096 x 11008 162 -> 72);
+//     that (8192 x 4096 23.0, Q6_K 4096 x 11008 162 -> 72); no split past
+//     256 64-row tiles, where 128 x 64 tiles already fill the chip (Q4_K
+//     22016 x 4096 37.4 against 49.8 split, Q6_K 128256 x 4096 269 against 330);
 //   * more tokens: 256 x 128 tiles when they cover 128 to 256 CUs once,
 //     128 x 128 past that, 128 x 64 below (Q4_K 4096 x 4096 at 512 tokens
 //     62 -> 37); 32-row split-K tiles when even 128 x 64 tiles are fewer than
@@ -662,7 +664,10 @@ int gemm_tile_config(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x
 #endif
   const int64_t t128x64 = (rows + 127) / 128 * ((n_tok + 63) / 64);
   if (x_f16) {
-    if (n_tok <= 64) return (rows + 31) / 32 > 256 ? 4 : 3;
+    if (n_tok <= 64) {
+      if ((rows + 63) / 64 > 256) return 2;  // enough 128-row tiles: no split
+      return (rows + 31) / 32 > 256 ? 4 : 3;
+    }
     if (t128x64 < 128) return 3;
     if (type == GQ_Q6_K && t128x64 <= 256) return 5;
   }
