@@ -11,10 +11,13 @@ blobs resident in HBM.
 Method:
   * weights: synthetic N(0, 0.02^2) fp32, one seeded draw per original matrix,
     quantized on the GPU by the library's quantizer; x ~ N(0, 1) fp32;
-  * each step is a HIP graph of the four launches; steps rotate over distinct
-    copies of the layer (>= 640 MB) so no step finds its weights in the 256 MB
-    Infinity Cache; timed region: synchronize, K graph replays, synchronize,
-    HIP events on the replay stream;
+  * steps rotate over distinct copies of the layer (>= 640 MB) so no step
+    finds its weights in the 256 MB Infinity Cache; the K timed steps run as
+    replays of HIP graphs holding 32 consecutive steps each, the way a decode
+    engine captures one token's pass over a 32-layer model as one graph (a
+    graph per single step adds ~5 us of replay boundary to every step);
+    timed region: synchronize, the replays, synchronize, HIP events on the
+    replay stream;
   * roofline: the dominant kernel (largest time per step) timed live with HIP
     events over graphs of 16 back-to-back launches of that kernel alone,
     rotating over >= 512 MB of copies; achieved = blob bytes per launch /
@@ -165,6 +168,49 @@ def time_graphs(graphs, steps, warmup):
     e0.record()
     for i in range(steps):
         graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+STEPS_PER_GRAPH = 32       # one decoded token of a 32-layer model
+
+
+def time_steps(step, ncopy, steps, warmup, per_graph=STEPS_PER_GRAPH):
+    """Average ms per step over `steps` steps, step i running step(sp, i %
+    ncopy), replayed as graphs of per_graph consecutive steps (the last graph
+    holds the remainder)."""
+    import torch
+    if steps < 1:
+        raise ValueError("steps must be >= 1")
+    g = min(per_graph, steps)
+    full, rem = divmod(steps, g)
+
+    def graph_of(first, count):
+        def fn(sp):
+            for k in range(count):
+                step(sp, (first + k) % ncopy)
+        return capture(fn)
+
+    # replay j covers steps j*g .. j*g+g-1: one graph per distinct first copy
+    by_off = {}
+    for j in range(full):
+        off = (j * g) % ncopy
+        if off not in by_off:
+            by_off[off] = graph_of(off, g)
+    tail = graph_of((full * g) % ncopy, rem) if rem else None
+    order = [by_off[(j * g) % ncopy] for j in range(full)]
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for i in range(warmup):                      # exactly `warmup` steps, plain launches
+        step(sp, i % ncopy)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for gr in order:
+        gr.replay()
+    if tail is not None:
+        tail.replay()
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
@@ -439,18 +485,15 @@ def fused_layer(mats, steps, warmup):
         if rc:
             raise RuntimeError(f"gq_matmul_decode({m.name}) failed: {gq.strerror(rc)}")
 
-    graphs = []
-    for ci in range(ncopy):
-        def fn(sp, ci=ci):
-            call(qkv.copies[ci].data_ptr(), None, qkv, qkv.rows, qkv.x.data_ptr(), qkv.xt,
-                 nw1.data_ptr(), qkv.y.data_ptr(), sp)
-            o.launch(ci, sp)
-            g = gu.copies[ci].data_ptr()
-            call(g, g + half, gu, gu.rows // 2, gu.x.data_ptr(), gu.xt, nw2.data_ptr(), h.data_ptr(), sp)
-            call(down.copies[ci].data_ptr(), None, down, down.rows, h.data_ptr(), gq.F32,
-                 None, down.y.data_ptr(), sp)
-        graphs.append(capture(fn))
-    return time_graphs(graphs, steps, warmup)
+    def step(sp, ci):
+        call(qkv.copies[ci].data_ptr(), None, qkv, qkv.rows, qkv.x.data_ptr(), qkv.xt,
+             nw1.data_ptr(), qkv.y.data_ptr(), sp)
+        o.launch(ci, sp)
+        g = gu.copies[ci].data_ptr()
+        call(g, g + half, gu, gu.rows // 2, gu.x.data_ptr(), gu.xt, nw2.data_ptr(), h.data_ptr(), sp)
+        call(down.copies[ci].data_ptr(), None, down, down.rows, h.data_ptr(), gq.F32,
+             None, down.y.data_ptr(), sp)
+    return time_steps(step, ncopy, steps, warmup)
 
 
 # Decode attention over a quantized KV cache: the 30B-class cache of the
@@ -593,15 +636,14 @@ def main():
         profile_launches(mats, args.profile_launches)
         return
 
-    step_graphs = []
-    for ci in range(ncopy):
-        def fn(sp, ci=ci):
-            for m in mats:
-                m.launch(ci, sp)
-        step_graphs.append(capture(fn))
+    def step(sp, ci):
+        for m in mats:
+            m.launch(ci, sp)
     log("timing the layer step")
-    ms = time_graphs(step_graphs, args.steps, args.warmup)
+    ms = time_steps(step, ncopy, args.steps, args.warmup)
     value = layer_bytes / (ms * 1e-3) / 1e9
+    ms1 = time_steps(step, ncopy, args.steps, args.warmup, per_graph=1)
+    log(f"  {ms*1e3:.2f} us/step in {STEPS_PER_GRAPH}-step graphs, {ms1*1e3:.2f} us in one-step graphs")
 
     log("timing the fused layer step")
     fms = fused_layer(mats, args.steps, args.warmup)
@@ -677,7 +719,11 @@ def main():
         "config": {"workload": "Llama-7B-shaped decode layer, Q4_K_M mix, batch 1",
                    "launches": [f"{n} {t} {sum(r for _, r in p)}x{c}" for n, t, p, c in LAYER],
                    "layer_blob_bytes": layer_bytes, "n_tok": 1, "x_dtype": "f32",
-                   "rotating_copies": ncopy, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+                   "rotating_copies": ncopy, "steps_per_graph": STEPS_PER_GRAPH,
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2)},
+        "one_step_graphs": {"ms_per_step": round(ms1, 5),
+                            "GBps": round(layer_bytes / (ms1 * 1e-3) / 1e9, 1),
+                            "what": "the same steps replayed as one graph per step"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
