@@ -25,8 +25,8 @@ _BUILD = os.path.join(_HERE, "_build")
 
 # This project's own type numbering (the pages give none).
 TYPES = {"f32": 0, "f16": 1, "q4_0": 2, "q5_0": 3, "q8_0": 4, "q4_k": 5, "q6_k": 6,
-         "q4_1": 7, "q5_k": 8}
-QUANT_TYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k"]
+         "q4_1": 7, "q5_k": 8, "q2_k": 9, "q3_k": 10}
+QUANT_TYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k", "q2_k", "q3_k"]
 
 
 def _lib_path(plant: int) -> str:

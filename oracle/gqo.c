@@ -56,6 +56,19 @@
  *     field is bit 4 of element e's code (as Q5_0's qh word, R3); q in
  *     [0, 31], w = (d*sc_i)*q - dmin*m_i in the fp32 order of R6.  176
  *     bytes = 5.5 bpw, Q4_K's 4.5 plus the fifth bit.
+ *  R16 Q2_K (256-weight super-block at 2.5-2.6 bpw [LC table]): Q4_K's
+ *     two-level recipe at 2 bits, d @0, dmin @2, scales[16] @4 (byte s:
+ *     low nibble = scale, high nibble = min of the 16-weight sub-block s),
+ *     qs[64] @20: byte 8g+k holds elements 32g+k+8u at bits 2u..2u+1 (the
+ *     2-bit plane order of R4's high parts); q in [0, 3], w = (d*sc_s)*q -
+ *     dmin*m_s in the fp32 order of R6.  84 bytes = 2.625 bpw.
+ *  R17 Q3_K (256-weight super-block at 3.4-4.0 bpw [LC table]): symmetric
+ *     like Q6_K, d @0, scales[12] @2 (16 unsigned six-bit fields in R1's
+ *     96-bit stream, field s = scale of the 16-weight sub-block s), ql[64]
+ *     @14 (low 2 bits of each code in R16's plane order), qh[32] @78 (bit e
+ *     of the little-endian 256-bit plane = bit 2 of element e's code, as
+ *     R15's fifth bits); q in [0, 7], w = d*(sc_s*(q-4)) with the integer
+ *     formed first (exact).  110 bytes = 3.4375 bpw.
  *  R13 Quantized KV cache: K and V are each [kv_len][n_kv][head_dim], row
  *     (t, g) = t*n_kv + g quantized along head_dim in blocks of the cache's
  *     type (the page's cache tensor is [batch, positions, kv heads, head
@@ -69,7 +82,9 @@
  *     its codes clamp at the ends of their range.  Q4_1: m is the largest
  *     fp16 <= the block minimum (saturating at -65504), d the cover of
  *     (max - m)/15, q = clamp(rnd((w - m)/d), 0, 15).  Q5_K: as Q4_K with 31
- *     levels per sub-block instead of 15.
+ *     levels per sub-block instead of 15.  Q2_K: as Q4_K over 16-weight
+ *     sub-blocks with 3 levels and 15-level scale and min fields.  Q3_K: as
+ *     Q6_K with codes clamp(rnd(w/step), -3, 3) + 4 and 63-level scales.
  */
 #include "gqo.h"
 #include <math.h>
@@ -86,7 +101,10 @@
  *   10 query head h reads KV head h % n_kv instead of h / n_rep,
  *   11 a block scale with no finite cover is stored as Inf,
  *   12 Q4_1 min subtracted instead of added,
- *   13 Q5_K fifth bits read from element e ^ 1. */
+ *   13 Q5_K fifth bits read from element e ^ 1,
+ *   14 Q2_K scale and min nibbles swapped,
+ *   15 Q3_K code offset 3 instead of 4,
+ *   16 Q2_K / Q3_K 2-bit plane read with k and u swapped. */
 #ifndef GQO_PLANT
 #define GQO_PLANT 0
 #endif
@@ -162,6 +180,8 @@ int gqo_block_info(int type, int64_t *qk, int64_t *bb) {
     case GQO_Q6_K: k = 256; b = 210; break;   /* 2+16+128+64 (R4) */
     case GQO_Q4_1: k = 32;  b = 20;  break;   /* 2 + 2 + 16  (R14) */
     case GQO_Q5_K: k = 256; b = 176; break;   /* 2+2+12+32+128 (R15) */
+    case GQO_Q2_K: k = 256; b = 84;  break;   /* 2+2+16+64   (R16) */
+    case GQO_Q3_K: k = 256; b = 110; break;   /* 2+12+64+32  (R17) */
     default: return -1;
     }
     if (qk) *qk = k;
@@ -185,9 +205,21 @@ typedef struct {
     double d, dmin;        /* fp16 scales as exact doubles; dmin: Q4_K and Q5_K's
                               super-min, Q4_1's min m */
     uint16_t d16, dmin16;
-    int sc[16], mn[16];    /* Q4_K: 8 scale + 8 min 6-bit fields; Q6_K: 16 int8 scales */
+    int sc[16], mn[16];    /* Q4_K: 8 scale + 8 min 6-bit fields; Q6_K: 16 int8 scales;
+                              Q2_K: 16 four-bit scales and mins; Q3_K: 16 six-bit scales */
     int q[256];
 } block_t;
+
+/* 64 bytes of 2-bit fields for 256 elements: byte 8g+k holds elements
+ * 32g+k+8u at bits 2u..2u+1 (R16, R17; R4's high-part order). */
+static void unpack_2bit_plane(const uint8_t *p, int *q) {
+    for (int g = 0; g < 8; g++)
+        for (int k = 0; k < 8; k++)
+            for (int u = 0; u < 4; u++) {
+                const int e = (GQO_PLANT == 16) ? 32 * g + 4 * k + u : 32 * g + k + 8 * u;
+                q[e] = (p[8 * g + k] >> (2 * u)) & 3;
+            }
+}
 
 static void unpack_block(int type, const uint8_t *b, block_t *o) {
     o->d16 = rd16(b);
@@ -250,6 +282,29 @@ static void unpack_block(int type, const uint8_t *b, block_t *o) {
             }
         break;
     }
+    case GQO_Q2_K:                           /* R16 */
+        o->dmin16 = rd16(b + 2);
+        o->dmin = gqo_half_to_double(o->dmin16);
+        for (int s = 0; s < 16; s++) {
+            const int lo = b[4 + s] & 0x0F, hi = b[4 + s] >> 4;
+            o->sc[s] = (GQO_PLANT == 14) ? hi : lo;
+            o->mn[s] = (GQO_PLANT == 14) ? lo : hi;
+        }
+        unpack_2bit_plane(b + 20, o->q);
+        break;
+    case GQO_Q3_K: {                         /* R17 */
+        for (int k = 0; k < 16; k++) {       /* R1's 96-bit stream of six-bit fields */
+            int v = 0;
+            for (int t = 0; t < 6; t++) {
+                int bit = 6 * k + t;
+                v |= ((b[2 + bit / 8] >> (bit % 8)) & 1) << t;
+            }
+            o->sc[k] = v;
+        }
+        unpack_2bit_plane(b + 14, o->q);
+        for (int e = 0; e < 256; e++) o->q[e] |= ((b[78 + e / 8] >> (e % 8)) & 1) << 2;
+        break;
+    }
     case GQO_Q6_K: {                         /* R4 */
         for (int s = 0; s < 16; s++) o->sc[s] = (int)(int8_t)b[2 + s];
         for (int g = 0; g < 8; g++) {
@@ -295,6 +350,17 @@ static float deq_f32(int type, const block_t *o, int j) {
         int k = o->sc[j / 16] * (o->q[j] - ((GQO_PLANT == 4) ? 31 : 32));  /* integer first */
         return d * (float)k;                           /* exact */
     }
+    case GQO_Q2_K: {                                   /* R16 */
+        int i = j / 16;
+        float a = d * (float)o->sc[i];                 /* exact */
+        float b = (float)o->dmin * (float)o->mn[i];    /* exact */
+        float t = a * (float)o->q[j];                  /* exact */
+        return t - b;                                  /* the one rounding */
+    }
+    case GQO_Q3_K: {                                   /* R17 */
+        int k = o->sc[j / 16] * (o->q[j] - ((GQO_PLANT == 15) ? 3 : 4));   /* integer first */
+        return d * (float)k;                           /* exact */
+    }
     }
     return NAN;
 }
@@ -315,6 +381,10 @@ static double deq_f64(int type, const block_t *o, int j) {
         return (o->d * (double)o->sc[i]) * (double)o->q[j] + ((GQO_PLANT == 2) ? m : -m);
     }
     case GQO_Q6_K: return o->d * ((double)o->sc[j / 16] * (double)(o->q[j] - ((GQO_PLANT == 4) ? 31 : 32)));
+    case GQO_Q2_K:                             /* R16: (d*sc)*q - dmin*m per 16 weights */
+        return (o->d * (double)o->sc[j / 16]) * (double)o->q[j] - o->dmin * (double)o->mn[j / 16];
+    case GQO_Q3_K:                             /* R17: d*(sc*(q-4)) */
+        return o->d * ((double)o->sc[j / 16] * (double)(o->q[j] - ((GQO_PLANT == 15) ? 3 : 4)));
     }
     return NAN;
 }
@@ -511,6 +581,16 @@ static void quant_sym32(const float *w, int L, int off, uint16_t *d16, int *q) {
         q[j] = (d == 0.0) ? off : clampi(rnd_away((double)w[j] / d), -L, L) + off;
 }
 
+/* Inverse of unpack_2bit_plane for codes in 0..3. */
+static void pack_2bit_plane(const int *q, uint8_t *p) {
+    for (int g = 0; g < 8; g++)
+        for (int k = 0; k < 8; k++) {
+            int v = 0;
+            for (int u = 0; u < 4; u++) v |= (q[32 * g + k + 8 * u] & 3) << (2 * u);
+            p[8 * g + k] = (uint8_t)v;
+        }
+}
+
 static void quant_block(int type, const float *w, uint8_t *b) {
     int q[256];
     memset(b, 0, 210);
@@ -603,6 +683,74 @@ static void quant_block(int type, const float *w, uint8_t *b) {
                 b[qs + 16 * i + k] = (uint8_t)((q[32 * i + k] & 15) | ((q[32 * i + k + 16] & 15) << 4));
         if (type == GQO_Q5_K)                             /* R15 */
             for (int e = 0; e < 256; e++) b[16 + e / 8] |= (uint8_t)(((q[e] >> 4) & 1) << (e % 8));
+        break;
+    }
+    case GQO_Q2_K: {      /* min/scale per 16-weight sub-block, two-level (R16, R7) */
+        double hi[16], M[16], Mp[16], sp[16];
+        double maxM = 0.0, maxs = 0.0;
+        for (int s = 0; s < 16; s++) {
+            double lo = 0.0, h = -INFINITY;
+            for (int j = 0; j < 16; j++) {
+                double v = (double)w[16 * s + j];
+                if (v < lo) lo = v;
+                if (v > h) h = v;
+            }
+            hi[s] = h;
+            M[s] = -lo;                                   /* >= 0: mins are unsigned */
+            if (M[s] > maxM) maxM = M[s];
+        }
+        uint16_t dmin16 = cover_scale(maxM, 15.0);
+        double dmin = gqo_half_to_double(dmin16);
+        int mn[16], sc[16];
+        for (int s = 0; s < 16; s++) {
+            mn[s] = (dmin == 0.0) ? 0 : clampi(ceil(M[s] / dmin), 0, 15);
+            Mp[s] = dmin * (double)mn[s];                 /* >= M[s] */
+            sp[s] = (hi[s] + Mp[s]) / 3.0;
+            if (sp[s] > maxs) maxs = sp[s];
+        }
+        uint16_t d16 = cover_scale(maxs, 15.0);
+        double d = gqo_half_to_double(d16);
+        for (int s = 0; s < 16; s++) {
+            sc[s] = (d == 0.0) ? 0 : clampi(ceil(sp[s] / d), 0, 15);
+            double step = d * (double)sc[s];
+            for (int j = 0; j < 16; j++)
+                q[16 * s + j] = (step == 0.0) ? 0
+                    : clampi(rnd_away(((double)w[16 * s + j] + Mp[s]) / step), 0, 3);
+        }
+        wr16(b, d16);
+        wr16(b + 2, dmin16);
+        for (int s = 0; s < 16; s++) b[4 + s] = (uint8_t)(sc[s] | (mn[s] << 4));
+        pack_2bit_plane(q, b + 20);
+        break;
+    }
+    case GQO_Q3_K: {      /* symmetric per 16-weight sub-block, two-level (R17, R7) */
+        double t[16], maxt = 0.0;
+        for (int s = 0; s < 16; s++) {
+            double a = 0.0;
+            for (int j = 0; j < 16; j++) if (fabs((double)w[16 * s + j]) > a) a = fabs((double)w[16 * s + j]);
+            t[s] = a / 3.0;
+            if (t[s] > maxt) maxt = t[s];
+        }
+        uint16_t d16 = cover_scale(maxt, 63.0);
+        double d = gqo_half_to_double(d16);
+        int sc[16];
+        for (int s = 0; s < 16; s++) {
+            sc[s] = (d == 0.0) ? 0 : clampi(ceil(t[s] / d), 0, 63);
+            double step = d * (double)sc[s];
+            for (int j = 0; j < 16; j++)
+                q[16 * s + j] = (step == 0.0) ? 4
+                    : clampi(rnd_away((double)w[16 * s + j] / step), -3, 3) + 4;
+        }
+        wr16(b, d16);
+        for (int k = 0; k < 16; k++)                      /* R1's stream */
+            for (int u = 0; u < 6; u++) {
+                int bit = 6 * k + u;
+                b[2 + bit / 8] |= (uint8_t)(((sc[k] >> u) & 1) << (bit % 8));
+            }
+        int lo2[256];
+        for (int e = 0; e < 256; e++) lo2[e] = q[e] & 3;
+        pack_2bit_plane(lo2, b + 14);
+        for (int e = 0; e < 256; e++) b[78 + e / 8] |= (uint8_t)(((q[e] >> 2) & 1) << (e % 8));
         break;
     }
     case GQO_Q6_K: {      /* symmetric per 16-weight sub-block, two-level */

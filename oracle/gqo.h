@@ -10,7 +10,8 @@
  * number of blocks, null pointer).
  *
  * Type codes (this project's own numbering; the pages give none):
- *   0 F32, 1 F16, 2 Q4_0, 3 Q5_0, 4 Q8_0, 5 Q4_K, 6 Q6_K, 7 Q4_1, 8 Q5_K
+ *   0 F32, 1 F16, 2 Q4_0, 3 Q5_0, 4 Q8_0, 5 Q4_K, 6 Q6_K, 7 Q4_1, 8 Q5_K, 9 Q2_K,
+ *   10 Q3_K
  */
 #ifndef GQO_H
 #define GQO_H
@@ -21,7 +22,8 @@ extern "C" {
 #endif
 
 enum { GQO_F32 = 0, GQO_F16 = 1, GQO_Q4_0 = 2, GQO_Q5_0 = 3, GQO_Q8_0 = 4,
-       GQO_Q4_K = 5, GQO_Q6_K = 6, GQO_Q4_1 = 7, GQO_Q5_K = 8 };
+       GQO_Q4_K = 5, GQO_Q6_K = 6, GQO_Q4_1 = 7, GQO_Q5_K = 8, GQO_Q2_K = 9,
+       GQO_Q3_K = 10 };
 
 /* Weights per block and bytes per block of a quantized type. */
 int gqo_block_info(int type, int64_t *block_elems, int64_t *block_bytes);

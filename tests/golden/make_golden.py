@@ -235,6 +235,76 @@ def q5_k():
     })
 
 
+def plane2(codes):
+    """64 bytes of 2-bit fields: byte 8g+k holds elements 32g+k+8u at bits 2u..2u+1."""
+    out = bytearray()
+    for g in range(8):
+        for k in range(8):
+            v = 0
+            for u in range(4):
+                c = codes[32 * g + k + 8 * u]
+                assert 0 <= c < 4
+                v |= c << (2 * u)
+            out.append(v)
+    return bytes(out)
+
+
+def q2_k():
+    d, dmin = Fraction(1, 64), Fraction(3, 512)
+    sc = [15 - s for s in range(16)]                      # 15 .. 0
+    mn = [(7 * s + 3) % 16 for s in range(16)]
+    codes = [(7 * e + e // 32) % 4 for e in range(256)]
+    raw = struct.pack("<HH", f16_bits_of(d), f16_bits_of(dmin))
+    raw += bytes(sc[s] | (mn[s] << 4) for s in range(16))
+    raw += plane2(codes)
+    assert len(raw) == 84
+    exp = [(d * sc[e // 16]) * codes[e] - dmin * mn[e // 16] for e in range(256)]
+    dump("q2_k_fields.json", {
+        "type": "q2_k",
+        "citation": "12 — llama.cpp / GGUF, table 'Other k-quants at a glance': Q2_K at "
+                    "2.5-2.6 bits per weight over a 256-weight super-block; the layout is "
+                    "not on the pages. Reading: the two-level scale/min recipe of "
+                    "Hitchhiker's Guide §11.2 at 2 bits: fp16 d, fp16 dmin, 16 bytes whose "
+                    "low nibble is the scale and high nibble the min of a 16-weight "
+                    "sub-block, then 64 bytes of 2-bit codes, byte 8g+k holding elements "
+                    "32g+k+8u at bits 2u..2u+1; w = (d*sc)*q - dmin*m with q in 0..3; "
+                    "84 B = 2.625 bpw.",
+        "fields": {"d": str(d), "dmin": str(dmin), "sc": sc, "m": mn, "codes": codes},
+        "hex": raw.hex(),
+        "expected": [float(v) for v in exp],
+        "expected_f32": [frac_f32(v) for v in exp],
+    })
+
+
+def q3_k():
+    d = Fraction(1, 32)
+    sc = [63, 0] + [4 * s + 1 for s in range(14)]
+    codes = [(3 * e + e // 16) % 8 for e in range(256)]
+    raw = struct.pack("<H", f16_bits_of(d)) + pack6(sc)
+    raw += plane2([c & 3 for c in codes])
+    qh = 0
+    for e, c in enumerate(codes):
+        qh |= ((c >> 2) & 1) << e
+    raw += qh.to_bytes(32, "little")
+    assert len(raw) == 110
+    exp = [d * (sc[e // 16] * (codes[e] - 4)) for e in range(256)]
+    dump("q3_k_fields.json", {
+        "type": "q3_k",
+        "citation": "12 — llama.cpp / GGUF, table 'Other k-quants at a glance': Q3_K_S / _M "
+                    "/ _L at 3.4-4.0 bits per weight over a 256-weight super-block; the "
+                    "layout is not on the pages. Reading: symmetric like Q6_K: fp16 d, 16 "
+                    "unsigned six-bit scales (one per 16 weights) as one LSB-first 96-bit "
+                    "stream, 64 bytes of the codes' low 2 bits (byte 8g+k holding elements "
+                    "32g+k+8u at bits 2u..2u+1), then a 32-byte plane whose bit e is bit 2 "
+                    "of element e's code; w = d*(sc*(q-4)) with q in 0..7; 110 B = "
+                    "3.4375 bpw.",
+        "fields": {"d": str(d), "sc": sc, "codes": codes},
+        "hex": raw.hex(),
+        "expected": [float(v) for v in exp],
+        "expected_f32": [frac_f32(v) for v in exp],
+    })
+
+
 if __name__ == "__main__":
     q4_0()
     q8_0()
@@ -253,3 +323,5 @@ if __name__ == "__main__":
     q6_k()
     q4_1()
     q5_k()
+    q2_k()
+    q3_k()

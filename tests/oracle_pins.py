@@ -32,7 +32,7 @@ import numpy as np
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
-QTYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k"]
+QTYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k", "q2_k", "q3_k"]
 
 
 def golden_fixtures():
@@ -77,6 +77,14 @@ def pin_sizes(o):
     assert o.block_info("q4_1") == (32, 2 + 2 + 16)
     qk, bb = o.block_info("q5_k")
     assert qk == 256 and bb == 144 + 256 // 8 and 5.5 <= bb * 8 / qk <= 5.7
+    # Q2_K and Q3_K (same table: 2.5-2.6 and 3.4-4.0 bits per weight on
+    # 256-weight super-blocks): 2-bit codes with 4-bit scales and mins per 16
+    # weights plus fp16 d and dmin; 3-bit codes with 6-bit scales per 16
+    # weights plus fp16 d.
+    qk, bb = o.block_info("q2_k")
+    assert qk == 256 and bb == 2 + 2 + 16 + 64 and 2.5 <= round(bb * 8 / qk, 1) <= 2.6
+    qk, bb = o.block_info("q3_k")
+    assert qk == 256 and bb == 2 + 12 + 64 + 32 and 3.4 <= bb * 8 / qk <= 4.0
 
 
 def _exact_dot(w64, x):
@@ -155,7 +163,7 @@ def pin_q4k_structured(o):
 def pin_pow2_and_perm(o):
     """Doubling d (and dmin) doubles y exactly; permuting rows permutes y."""
     offs = {"q4_0": [0], "q5_0": [0], "q8_0": [0], "q4_k": [0, 2], "q6_k": [0], "q4_1": [0, 2],
-            "q5_k": [0, 2]}
+            "q5_k": [0, 2], "q2_k": [0, 2], "q3_k": [0]}
     for k, t in enumerate(QTYPES):
         qk, bb = o.block_info(t)
         rows, cols = 6, 2 * qk
@@ -208,9 +216,10 @@ def _roundtrip_bound(w: np.ndarray, t: str) -> np.ndarray:
         a = np.abs(w.reshape(-1, 32)).max(axis=1, keepdims=True)
         d = a / L * up + 2.0 ** -24
         return np.broadcast_to(d / 2, (a.shape[0], 32)).reshape(w.shape)
-    if t == "q6_k":
-        ts = np.abs(w.reshape(-1, 16, 16)).max(axis=2, keepdims=True) / 31.0
-        d = ts.max(axis=1, keepdims=True) / 127.0 * up + 2.0 ** -24             # [blocks,1,1]
+    if t in ("q6_k", "q3_k"):
+        L, F = (31.0, 127.0) if t == "q6_k" else (3.0, 63.0)
+        ts = np.abs(w.reshape(-1, 16, 16)).max(axis=2, keepdims=True) / L
+        d = ts.max(axis=1, keepdims=True) / F * up + 2.0 ** -24                 # [blocks,1,1]
         step = ts + d
         return np.broadcast_to(step / 2, (ts.shape[0], 16, 16)).reshape(w.shape)
     if t == "q4_1":
@@ -219,15 +228,17 @@ def _roundtrip_bound(w: np.ndarray, t: str) -> np.ndarray:
         span = (hi - lo) + np.abs(lo) * 2.0 ** -10 + 2.0 ** -24      # m is an fp16 <= lo
         d = span / 15.0 * up + 2.0 ** -24
         return np.broadcast_to(d / 2, b.shape).reshape(w.shape)
-    # q4_k, q5_k
-    L = 31.0 if t == "q5_k" else 15.0
-    sb = w.reshape(-1, 8, 32)
+    # q4_k, q5_k, q2_k
+    L = {"q5_k": 31.0, "q4_k": 15.0, "q2_k": 3.0}[t]
+    F = 15.0 if t == "q2_k" else 63.0              # levels of the scale and min fields
+    n = 16 if t == "q2_k" else 8                   # sub-blocks per super-block
+    sb = w.reshape(-1, n, 256 // n)
     lo = np.minimum(sb.min(axis=2), 0.0)
     hi = sb.max(axis=2)
     M = -lo
-    dmin = M.max(axis=1, keepdims=True) / 63.0 * up + 2.0 ** -24
+    dmin = M.max(axis=1, keepdims=True) / F * up + 2.0 ** -24
     sp = (hi + M + dmin) / L
-    d = sp.max(axis=1, keepdims=True) / 63.0 * up + 2.0 ** -24
+    d = sp.max(axis=1, keepdims=True) / F * up + 2.0 ** -24
     step = sp + d
     return np.broadcast_to((step / 2)[..., None], sb.shape).reshape(w.shape)
 
@@ -264,7 +275,8 @@ def pin_quantize_saturation(o):
     times the largest magnitude the type can represent."""
     top = 65504.0
     big = {"q4_0": top * 7, "q5_0": top * 15, "q8_0": top * 127, "q6_k": top * 127 * 31,
-           "q4_k": top * 63 * 15, "q5_k": top * 63 * 31, "q4_1": top * 16}
+           "q4_k": top * 63 * 15, "q5_k": top * 63 * 31, "q4_1": top * 16,
+           "q2_k": top * 15 * 3, "q3_k": top * 63 * 3}
     for t in QTYPES:
         qk, _ = o.block_info(t)
         ramp = np.linspace(-1.0, 1.0, qk)
@@ -286,6 +298,15 @@ def pin_quantize_saturation(o):
         elif t == "q6_k":
             assert int(blob[2]) == 127 and int(blob[2 + 15]) == 127, t      # scales clamp at 127
             assert w64[0] == -big[t] and w64[-1] == big[t], t
+        elif t == "q2_k":
+            # min and scale fields clamp at 15: sub-block 0 all negative ends at
+            # code 0 under min 15, sub-block 15 all positive at code 3, scale 15
+            assert _f16_field(blob, 2) == 0x7BFF, (t, "dmin")
+            assert int(blob[4]) >> 4 == 15 and int(blob[4 + 15]) & 15 == 15, t
+            assert w64[0] == -top * 15 and w64[-1] == big[t], (t, w64[0], w64[-1])
+        elif t == "q3_k":
+            assert int(blob[2]) & 63 == 63, t                                # scale 0 at 63
+            assert w64[0] == -big[t] and w64[-1] == big[t], (t, w64[0], w64[-1])
         else:
             assert w64[0] == -big[t] and w64[-1] == big[t], (t, w64[0], w64[-1])
         assert np.all(np.abs(w64) <= big[t]), t

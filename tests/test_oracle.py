@@ -18,7 +18,8 @@ PLANTS = {1: "nibble order swapped", 2: "Q4_K min sign", 3: "Q4_K scale/min swap
           7: "RMSNorm drops eps", 8: "SiLU exponent sign",
           9: "attention without 1/sqrt(head_dim)", 10: "attention head mapping h % n_kv",
           11: "unsaturated (Inf) block scale", 12: "Q4_1 min sign",
-          13: "Q5_K fifth bits of the neighbouring element"}
+          13: "Q5_K fifth bits of the neighbouring element", 14: "Q2_K scale/min nibbles swapped",
+          15: "Q3_K code offset 3", 16: "2-bit code plane in element order"}
 
 
 @pytest.mark.parametrize("plant", sorted(PLANTS), ids=lambda k: PLANTS[k])
@@ -80,7 +81,7 @@ def test_quantize_rejects_bad_shapes(oracle):
     with pytest.raises(ValueError):
         o.quantize(np.zeros((2, 100), np.float32), "q4_k")
     with pytest.raises(ValueError):
-        o.block_info("q3_k")
+        o.block_info("iq4_xs")
 
 
 def test_matmul_zero_tokens(oracle):
