@@ -437,8 +437,9 @@ def sweep(steps):
     cases = [("single q4_k 2048x2048", "q4_k", [("w", 2048)], 2048, 1, "f32")]
     cases += [(f"per-type {t} {r}x{c}", t, [(n, r)], c, 1, "f32") for n, t, r, c in synth.PER_TYPE_SWEEP_4096]
     cases += [(f"q4_k 11008x4096 n={n} f16", "q4_k", [("w", 11008)], 4096, n, "f16") for n in synth.GEMM_TOKENS]
-    for t in ("q4_1", "q5_k"):
+    for t in ("q4_1", "q5_k", "q2_k", "q3_k"):
         cases += [(f"{t} 4096x4096 n=1", t, [("w", 4096)], 4096, 1, "f32"),
+                  (f"{t} 4096x4096 n=64 f16", t, [("w", 4096)], 4096, 64, "f16"),
                   (f"{t} 4096x4096 n=512 f16", t, [("w", 4096)], 4096, 512, "f16")]
     for n in synth.LLAMA3_8B_TOKENS:
         for name, t, r, c in synth.LLAMA3_8B_LAYER_Q4KM:

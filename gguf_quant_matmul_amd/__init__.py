@@ -16,10 +16,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgq.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "gq.h")
 
-F32, F16, Q4_0, Q5_0, Q8_0, Q4_K, Q6_K, Q4_1, Q5_K = range(9)
+F32, F16, Q4_0, Q5_0, Q8_0, Q4_K, Q6_K, Q4_1, Q5_K, Q2_K, Q3_K = range(11)
 TYPES = {"f32": F32, "f16": F16, "q4_0": Q4_0, "q5_0": Q5_0, "q8_0": Q8_0,
-         "q4_k": Q4_K, "q6_k": Q6_K, "q4_1": Q4_1, "q5_k": Q5_K}
-QUANT_TYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k"]
+         "q4_k": Q4_K, "q6_k": Q6_K, "q4_1": Q4_1, "q5_k": Q5_K, "q2_k": Q2_K, "q3_k": Q3_K}
+QUANT_TYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k", "q2_k", "q3_k"]
 
 _lib = None
 

@@ -22,7 +22,7 @@ constexpr int64_t kStreamOnly = 32;               // n_tok up to this: always th
 constexpr int64_t kMaxElems = (int64_t)1 << 40;   // dequant / quantize grid.x < 2^31
 constexpr int64_t kMaxCacheBytes = 0x7FFF0000;    // KV caches: below the kernels' out-of-range offset
 
-bool quant_type(int t) { return t >= GQ_Q4_0 && t <= GQ_Q5_K; }
+bool quant_type(int t) { return t >= GQ_Q4_0 && t <= GQ_Q3_K; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -48,11 +48,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? GQ_OK : GQ_EHIP; }
 // its time is ~ rounds of resident tiles x K steps x step time (its own
 // estimate, by tile shape), while the weight-stream kernel's time grows with
 // the number of 16-token passes: measured on MI355X, a pass streams
-// rows*cols weights at ~150 (Q6_K ~165, the 32-weight types ~80) TFLOP/s.  The batch goes to the
+// rows*cols weights at ~150 (Q4_K, Q5_K, Q2_K, Q3_K; Q6_K ~165, the 32-weight
+// types ~80) TFLOP/s.  The batch goes to the
 // weight-stream kernel, in ceil(n/64) near-equal chunks of at most 64 tokens,
 // when that estimate is lower.
 bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16) {
-  const double rate = (type == GQ_Q4_K || type == GQ_Q5_K) ? 150e12 : (type == GQ_Q6_K) ? 165e12 : 80e12;
+  const double rate = (type == GQ_Q4_K || type == GQ_Q5_K || type == GQ_Q2_K || type == GQ_Q3_K)
+                          ? 150e12
+                          : (type == GQ_Q6_K) ? 165e12 : 80e12;
   const double gemm_us = gq::gemm_estimate_us(type, rows, cols, n_tok, x_f16);
   const double pass_us = (double)rows * (double)cols * 32.0 / rate * 1e6;
   const int64_t k = (n_tok + 63) / 64, base = n_tok / k, extra = n_tok % k;
@@ -77,6 +80,8 @@ int gq_type_info(int type, int64_t* block_elems, int64_t* block_bytes) {
     case GQ_Q6_K: qk = 256; bb = 210; break;
     case GQ_Q4_1: qk = 32;  bb = 20;  break;
     case GQ_Q5_K: qk = 256; bb = 176; break;
+    case GQ_Q2_K: qk = 256; bb = 84;  break;
+    case GQ_Q3_K: qk = 256; bb = 110; break;
     default: return GQ_EINVAL_TYPE;
   }
   if (block_elems) *block_elems = qk;

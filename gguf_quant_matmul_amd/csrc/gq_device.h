@@ -126,6 +126,8 @@ template <> struct Geo<GQ_Q4_K> { static constexpr int QK = 256, BB = 144; };
 template <> struct Geo<GQ_Q6_K> { static constexpr int QK = 256, BB = 210; };
 template <> struct Geo<GQ_Q4_1> { static constexpr int QK = 32,  BB = 20;  };
 template <> struct Geo<GQ_Q5_K> { static constexpr int QK = 256, BB = 176; };
+template <> struct Geo<GQ_Q2_K> { static constexpr int QK = 256, BB = 84;  };
+template <> struct Geo<GQ_Q3_K> { static constexpr int QK = 256, BB = 110; };
 
 // A "segment" is 32 consecutive weights of a row: one block of the 32-weight
 // types, one sub-block of Q4_K, one 32-weight group of Q6_K.  Segment s of a
@@ -166,6 +168,18 @@ __device__ __forceinline__ uint32_t spread4_bit4(uint32_t v) {
 // bits b + 7k (k = 0..3), all distinct, so no carries; bit 8b is the k = b copy.
 __device__ __forceinline__ uint32_t bits_to_b4(uint32_t v4) {
   return (((v4 & 0xFu) * 0x00204081u) & 0x01010101u) << 4;   // a 24-bit multiply
+}
+
+// Bit b (b = 0..3) of v4 to bit 2 of byte b (Q3_K's third bits).
+__device__ __forceinline__ uint32_t bits_to_b2(uint32_t v4) {
+  return (((v4 & 0xFu) * 0x00204081u) & 0x01010101u) << 2;
+}
+
+// Q2_K / Q3_K 2-bit plane: byte 8g+k holds elements 32g+k+8u at bits
+// 2u..2u+1, so the codes of elements 8u .. 8u+7 of group g are bits 2u..2u+1
+// of the group's 8 bytes (w0 = bytes 0..3, w1 = bytes 4..7), one per byte.
+__device__ __forceinline__ uint32_t plane2(uint32_t w, int u) {
+  return (w >> (2 * u)) & 0x03030303u;
 }
 
 // fp16 pair {RNE_fp16(c0 s + nb), RNE_fp16(c1 s + nb)} for codes held in

@@ -222,6 +222,72 @@ template <> struct BR<GQ_Q6_K> {
     }
   }
 };
+// Q2_K: the segment (32-weight group G of a super-block) is 16-weight
+// sub-blocks 2G, 2G+1; its codes are bits 2c..2c+1 of the group's 8 plane
+// bytes for elements 8c .. 8c+7, so chunk c shifts them down and masks two
+// 16-bit fields per dword (subnormal codes into the mixed FMA, as Q4_K).
+template <> struct BR<GQ_Q2_K> {
+  static constexpr bool kHeader = false;
+  uint32_t dm, sm;                           // d | dmin; scale/min bytes of 2G, 2G+1
+  u32x2 q;                                   // the group's 8 code bytes
+  template <bool HDR = true>
+  __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
+    const int vo = ok ? vrow + (sg >> 3) * 84 : kOobOff;
+    const int G = sg & 7;
+    dm = bld4(R, vo, 0);
+    sm = bld2(R, vo + 2 * G, 4);
+    q = bld8(R, vo + 8 * G, 20);
+  }
+  // largest |w| the fields allow: 15 * 3 |d| + 15 |dmin|
+  __device__ float bound() const { return fmaf(45.f, fabsf(h2f(dm)), 15.f * fabsf(h2f(dm >> 16))); }
+  __device__ void decode(int, int k, u32x4 out[4]) const {
+    const float d = __builtin_ldexpf(h2f(dm), k + 24), dmin = __builtin_ldexpf(h2f(dm >> 16), k);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {            // chunk c: elements 8c .. 8c+7
+      const uint32_t b = sm >> (8 * (c >> 1));   // sub-block 2G + c / 2
+      const float s = d * (float)(b & 15u), nb = -(dmin * (float)((b >> 4) & 15u));
+      const uint32_t w0 = q.x >> (2 * c), w1 = q.y >> (2 * c);
+      const uint32_t e0 = w0 & 0x00030003u, o0 = (w0 >> 8) & 0x00030003u;   // bytes 0, 2 / 1, 3
+      const uint32_t e1 = w1 & 0x00030003u, o1 = (w1 >> 8) & 0x00030003u;
+      out[c] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
+                     mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
+    }
+  }
+};
+// Q3_K: the segment's scale fields 2G, 2G+1 (12 bits of the 96-bit stream),
+// its 8 low-bit plane bytes and the 32 third bits; each code q = low | third
+// << 2 is a byte (fp16 subnormal in its 16-bit field), and the mixed FMA
+// rounds the exact a*(q-4) to fp16 once, a = d * sc.
+template <> struct BR<GQ_Q3_K> {
+  static constexpr bool kHeader = false;
+  uint32_t d, sc, qh;
+  u32x2 q;
+  template <bool HDR = true>
+  __device__ void load(__amdgpu_buffer_rsrc_t R, int vrow, int sg, bool ok) {
+    const int vo = ok ? vrow + (sg >> 3) * 110 : kOobOff;
+    const int G = sg & 7;
+    d = bld2(R, vo, 0);
+    sc = bld4(R, vo + ((12 * G) >> 3), 2);
+    q = bld8(R, vo + 8 * G, 14);
+    qh = bld4(R, vo + 4 * G, 78);
+  }
+  __device__ float bound() const { return 252.f * fabsf(h2f(d)); }   // |sc (q - 4)| <= 252
+  __device__ void decode(int sg, int k, u32x4 out[4]) const {
+    const float dd = __builtin_ldexpf(h2f(d), k);
+    const uint32_t f = sc >> ((12 * (sg & 7)) & 7);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {            // chunk c: elements 8c .. 8c+7
+      const float a = dd * (float)((f >> (6 * (c >> 1))) & 63u);
+      const float s = a * 16777216.f, nb = -4.f * a;   // a * (q - 4) is exact in fp32
+      const uint32_t v0 = plane2(q.x, c) | bits_to_b2(qh >> (8 * c));
+      const uint32_t v1 = plane2(q.y, c) | bits_to_b2(qh >> (8 * c + 4));
+      const uint32_t e0 = v0 & 0x00FF00FFu, o0 = (v0 >> 8) & 0x00FF00FFu;
+      const uint32_t e1 = v1 & 0x00FF00FFu, o1 = (v1 >> 8) & 0x00FF00FFu;
+      out[c] = u32x4{mixpair<0>(e0, o0, s, nb), mixpair<1>(e0, o0, s, nb),
+                     mixpair<0>(e1, o1, s, nb), mixpair<1>(e1, o1, s, nb)};
+    }
+  }
+};
 template <> struct BR<GQ_Q8_0> {
   static constexpr bool kHeader = false;
   u32x4 c0, c1;
@@ -682,7 +748,7 @@ int gemm_tile_config(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x
 // stretched by the tiles past one per CU.
 double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x_f16) {
   // per tile shape: rows, tokens, K groups, and a step's time per type
-  // (Q4_K / Q5_K, Q6_K, Q8_0 / Q5_0 / Q4_1, Q4_0)
+  // (Q4_K / Q5_K / Q2_K, Q6_K, Q8_0 / Q5_0 / Q4_1 / Q3_K, Q4_0)
   struct Cfg {
     int64_t bn, bm, ks;
     double step_us[4];
@@ -694,8 +760,8 @@ double gemm_estimate_us(int type, int64_t rows, int64_t cols, int64_t n_tok, boo
   int c = gemm_tile_config(type, rows, cols, n_tok, x_f16);
   if (c < 0 || c > 5) c = 0;
   const Cfg& f = cfg[c];
-  const int tc = (type == GQ_Q4_K || type == GQ_Q5_K) ? 0 : (type == GQ_Q6_K) ? 1
-                 : (type == GQ_Q4_0) ? 3 : 2;
+  const int tc = (type == GQ_Q4_K || type == GQ_Q5_K || type == GQ_Q2_K) ? 0
+                 : (type == GQ_Q6_K) ? 1 : (type == GQ_Q4_0) ? 3 : 2;
   const double tiles = (double)((rows + f.bn - 1) / f.bn * ((n_tok + f.bm - 1) / f.bm));
   const double steps = (double)(((cols + BK - 1) / BK + f.ks - 1) / f.ks);
   const double load = tiles > 256.0 ? tiles / 256.0 : 1.0;
@@ -716,6 +782,8 @@ hipError_t launch_gemm(int type, const void* blob, int64_t rows, int64_t cols, c
     GQ_GEMM_CASE(GQ_Q6_K)
     GQ_GEMM_CASE(GQ_Q4_1)
     GQ_GEMM_CASE(GQ_Q5_K)
+    GQ_GEMM_CASE(GQ_Q2_K)
+    GQ_GEMM_CASE(GQ_Q3_K)
 #undef GQ_GEMM_CASE
   }
   return hipErrorInvalidValue;

@@ -300,6 +300,77 @@ template <> struct Slice<GQ_Q5_K> {
   }
 };
 
+// Q2_K (quarter j of a super-block: 16-weight sub-blocks 4j..4j+3, 32-weight
+// groups 2j, 2j+1): d | dmin, the quarter's four scale/min bytes and its 16
+// code bytes.  Byte k of a group holds elements k + 8u at bits 2u; masked in
+// place, bit pair u is the fp16 subnormal 4^u q 2^-24, so one mixed FMA per
+// weight forms its product (powers of two undo the 4^u); factored
+// sub-block sums as Q4_K, a*sum(q*x) - b*sum(x) per 16 weights.
+template <> struct Slice<GQ_Q2_K> {
+  uint32_t dm, sm;
+  u32x4 q;
+  static __device__ int voff(int sl) { return (sl >> 2) * 84; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int j) {
+    dm = bld4(r, vo, 0);
+    sm = bld4(r, vo + 4 * j, 4);
+    q = bld16(r, vo + 16 * j, 20);
+  }
+  template <bool ASM>
+  __device__ float dot(int h, const float* x, const float* xs, int) const {
+    float s[4] = {0.f, 0.f, 0.f, 0.f};        // bit pair u: elements 8u .. 8u+7
+#pragma unroll
+    for (int c = 0; c < 2; c++) {             // bytes 4c .. 4c+3 of group 2j + h
+      const uint32_t lo = q[2 * h + c], hi = lo >> 8;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const uint32_t m = 0x00030003u << (2 * u);
+        s[u] = dot4mix(lo & m, hi & m, x + 4 * c + 8 * u, s[u]);
+      }
+    }
+    // sub-blocks 4j + 2h (elements 0..15 of the group) and 4j + 2h + 1
+    const uint32_t b0 = sm >> (16 * h), b1 = sm >> (16 * h + 8);
+    const float d = h2f(dm) * kSub, dmin = h2f(dm >> 16);
+    const float a0 = d * (float)(b0 & 15u), a1 = d * (float)(b1 & 15u);
+    const float m0 = dmin * (float)((b0 >> 4) & 15u), m1 = dmin * (float)((b1 >> 4) & 15u);
+    const float t0 = fmaf(s[1], 0.25f, s[0]), t1 = fmaf(s[3], 0.015625f, s[2] * 0.0625f);
+    return fmaf(a0, t0, -m0 * xs[0]) + fmaf(a1, t1, -m1 * xs[1]);
+  }
+};
+
+// Q3_K (quarter j: sub-blocks 4j..4j+3): d, the quarter's four scale fields
+// (24 bits of the 96-bit stream), 16 low-bit plane bytes and 64 third bits;
+// each code becomes the signed byte q - 4, so every product (q - 4) * x
+// carries only its own rounding (as Q6_K); per 16 weights sc * sum.
+template <> struct Slice<GQ_Q3_K> {
+  uint32_t d, sc;
+  u32x4 q;
+  u32x2 qh;
+  static __device__ int voff(int sl) { return (sl >> 2) * 110; }
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int j) {
+    d = bld2(r, vo, 0);
+    sc = bld4(r, vo + 3 * j, 2);              // fields 4j.. start at bit 24j
+    q = bld16(r, vo + 16 * j, 14);
+    qh = bld8(r, vo + 8 * j, 78);
+  }
+  template <bool ASM>
+  __device__ float dot(int h, const float* x, const float*, int) const {
+    const uint32_t H = h ? qh.y : qh.x;       // bit e: element e of group 2j + h
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; c++) {
+      const uint32_t w = q[2 * h + c];        // plane bytes 4c .. 4c+3
+#pragma unroll
+      for (int u = 0; u < 4; u++) {           // elements 4c + 8u .. +3
+        const uint32_t v = plane2(w, u) | bits_to_b2(H >> (4 * c + 8 * u));
+        if (u < 2) s0 = dot4s_asm(centre<4>(v), x + 4 * c + 8 * u, s0);
+        else s1 = dot4s_asm(centre<4>(v), x + 4 * c + 8 * u, s1);
+      }
+    }
+    const uint32_t f = sc >> (12 * h);        // fields 4j + 2h, 4j + 2h + 1
+    return h2f(d) * fmaf((float)((f >> 6) & 63u), s1, (float)(f & 63u) * s0);
+  }
+};
+
 // Physical float index in LDS of logical x index f: 16-byte chunk c of slice
 // s lands at chunk c ^ (s & 15), so 16 lanes reading chunk c of 16
 // consecutive slices hit 16 distinct groups of 4 banks.
@@ -636,6 +707,8 @@ hipError_t launch_gemv_fused(int type, const void* blob, const void* up_blob, in
     case GQ_Q6_K: return gemv_t<GQ_Q6_K>(blob, rows, cols, x, x_f16, y, fu, st);
     case GQ_Q4_1: return gemv_t<GQ_Q4_1>(blob, rows, cols, x, x_f16, y, fu, st);
     case GQ_Q5_K: return gemv_t<GQ_Q5_K>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q2_K: return gemv_t<GQ_Q2_K>(blob, rows, cols, x, x_f16, y, fu, st);
+    case GQ_Q3_K: return gemv_t<GQ_Q3_K>(blob, rows, cols, x, x_f16, y, fu, st);
   }
   return hipErrorInvalidValue;
 }

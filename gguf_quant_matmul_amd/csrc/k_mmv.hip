@@ -181,6 +181,28 @@ template <> struct WS<GQ_Q6_K> {     // slab = one super-block; 32-groups 2g, 2g
   }
 };
 
+template <> struct WS<GQ_Q2_K> {     // slab = one super-block; 16-weight sub-blocks 4g..4g+3
+  uint32_t dm, sm;                   // d | dmin; their scale/min bytes
+  u32x4 q;                           // code bytes of 32-groups 2g, 2g+1
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int g) {
+    dm = bld4(r, vo, 0);
+    sm = bld4(r, vo + 4 * g, 4);
+    q = bld16(r, vo + 16 * g, 20);
+  }
+};
+
+template <> struct WS<GQ_Q3_K> {     // slab = one super-block; sub-blocks 4g..4g+3
+  uint32_t d, sc;                    // d; scale fields 4g.. (24 bits)
+  u32x4 q;                           // low-bit plane bytes of groups 2g, 2g+1
+  u32x2 qh;                          // third bits of elements 64g .. 64g+63
+  __device__ void load(__amdgpu_buffer_rsrc_t r, int vo, int g) {
+    d = bld2(r, vo, 0);
+    sc = bld4(r, vo + 3 * g, 2);
+    q = bld16(r, vo + 16 * g, 14);
+    qh = bld8(r, vo + 8 * g, 78);
+  }
+};
+
 // 32-weight types: slab = 8 blocks of the row.  Lane group g loads blocks 2g
 // and 2g+1, each with whole dwords of its own bytes and a 2-byte tail (3 or
 // 4 loads per block, from a 2-byte-aligned start, none reaching past its
@@ -372,6 +394,76 @@ __device__ __forceinline__ void slab_mma(const uint8_t* xw, const uint8_t* ww, c
         acc[mt] -= dmin * Pm[mt];
       }
     }
+  } else if constexpr (T == GQ_Q2_K) {
+    // step j: columns 64g + 8j .. +7 = elements 8u .. 8u+7 (u = j % 4) of
+    // group 2g + j / 4, bits 2u..2u+1 of its 8 plane bytes; 16-weight
+    // sub-block 4g + 2 (j / 4) + u / 2.  B = sc * q (exact), the min term as
+    // a second product with m, both scaled by d and dmin in fp32.
+    const float d = h2f(ws.dm), dmin = h2f(ws.dm >> 16);
+    f32x4v Pk[MT], Pm[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) Pk[mt] = Pm[mt] = z;
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int gg = j >> 2, u = j & 3;
+      const uint32_t b = ws.sm >> (8 * (2 * gg + (u >> 1)));
+      const float sc = (float)(b & 15u), m = (float)((b >> 4) & 15u);
+      f16x2 v[4];
+      bytes8(kE1024, plane2(ws.q[2 * gg], u), plane2(ws.q[2 * gg + 1], u), v);   // 1024 + q
+      const f16x2 s2 = hpair(sc, sc), n2 = hpair(-1024.f * sc, -1024.f * sc);
+      const f16x8 B = cat8(__builtin_elementwise_fma(v[0], s2, n2), __builtin_elementwise_fma(v[1], s2, n2),
+                           __builtin_elementwise_fma(v[2], s2, n2), __builtin_elementwise_fma(v[3], s2, n2));
+      const _Float16 mh = (_Float16)m;
+      const f16x8 M = f16x8{mh, mh, mh, mh, mh, mh, mh, mh};
+#pragma unroll
+      for (int mt = 0; mt < MT; mt++) {
+        const f16x8 ah = read_a<P>(xw, t + 16 * mt, 8 * g + j);
+        Pk[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, B, Pk[mt], 0, 0, 0);
+        Pm[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, M, Pm[mt], 0, 0, 0);
+        if constexpr (XLO) {
+          const f16x8 al = read_a<P>(xw + P * 512, t + 16 * mt, 8 * g + j);
+          Pk[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, B, Pk[mt], 0, 0, 0);
+          Pm[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, M, Pm[mt], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      if constexpr (XLO) {
+        acc[mt] += (d * iv) * Pk[mt];
+        acc[mt] -= (dmin * iv) * Pm[mt];
+      } else {
+        acc[mt] += d * Pk[mt];
+        acc[mt] -= dmin * Pm[mt];
+      }
+    }
+  } else if constexpr (T == GQ_Q3_K) {
+    // step j as Q2_K; code q = low bits | third bit << 2, B = sc * (q - 4)
+    // exactly (|B| <= 252): (1024 + q) - 1028 is exact in fp16, then the
+    // product with sc
+    const float d = h2f(ws.d);
+    f32x4v Pk[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) Pk[mt] = z;
+    const f16x2 n4 = hpair(-1028.f, -1028.f);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const int gg = j >> 2, u = j & 3;
+      const uint32_t hb = (gg ? ws.qh.y : ws.qh.x) >> (8 * u);   // third bits of the 8 elements
+      const uint32_t c0 = plane2(ws.q[2 * gg], u) | bits_to_b2(hb);
+      const uint32_t c1 = plane2(ws.q[2 * gg + 1], u) | bits_to_b2(hb >> 4);
+      const float sc = (float)((ws.sc >> (6 * (2 * gg + (u >> 1)))) & 63u);
+      f16x2 v[4];
+      bytes8(kE1024, c0, c1, v);
+      const f16x2 s2 = hpair(sc, sc);
+      const f16x8 B = cat8((v[0] + n4) * s2, (v[1] + n4) * s2, (v[2] + n4) * s2, (v[3] + n4) * s2);
+      mma<XLO, P>(xw, t, 8 * g + j, B, Pk);
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; mt++) {
+      if constexpr (XLO) acc[mt] += (d * iv) * Pk[mt];
+      else acc[mt] += d * Pk[mt];
+    }
   } else if constexpr (T == GQ_Q6_K) {
     const float d = h2f(ws.d);
     f32x4v Pk[MT];
@@ -502,7 +594,8 @@ __global__ void __launch_bounds__(512) k_mmv(const uint8_t* __restrict__ blob, i
                                              int rb, const void* __restrict__ xv, int n,
                                              float* __restrict__ y, int tiles, int passes) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  constexpr bool KQ = (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K);
+  constexpr bool KQ = (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K || T == GQ_Q2_K ||
+                       T == GQ_Q3_K);
   constexpr int ES = XLO ? 4 : 2;
   constexpr int XB = P * 512 * (XLO ? 2 : 1);   // LDS bytes per wave: activations,
   constexpr int WB = kWB<T>;                    // then staged weights (32-weight types)
@@ -685,7 +778,7 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // slab, halving the activation reads, which there outweigh the weights'
   // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;
   // with fewer tiles the halved wave count costs more than it saves)
-  if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K) {
+  if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K || T == GQ_Q2_K || T == GQ_Q3_K) {
     if ((rows + 15) / 16 >= GQ_MMV_RT2_TILES)
       return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2), st);
   }
@@ -723,6 +816,8 @@ hipError_t launch_mmv(int type, const void* blob, int64_t rows, int64_t cols, co
     GQ_MMV_CASE(GQ_Q6_K)
     GQ_MMV_CASE(GQ_Q4_1)
     GQ_MMV_CASE(GQ_Q5_K)
+    GQ_MMV_CASE(GQ_Q2_K)
+    GQ_MMV_CASE(GQ_Q3_K)
 #undef GQ_MMV_CASE
   }
   return hipErrorInvalidValue;

@@ -61,6 +61,36 @@ __device__ __forceinline__ void seg_dequant(const uint8_t* row, int s, float w[3
       w[k] = t0 - bm;                          // one rounding
       w[k + 16] = t1 - bm;
     }
+  } else if constexpr (T == GQ_Q2_K) {
+    const int G = s & 7;                       // elements 32G .. 32G+31 of the super-block
+    const float d = h2f(ld2u(b)), dmin = h2f(ld2u(b + 2));
+    const uint8_t* qs = b + 20 + 8 * G;        // byte k: elements k + 8u at bits 2u
+#pragma unroll
+    for (int hh = 0; hh < 2; hh++) {           // 16-weight sub-blocks 2G, 2G+1
+      const int sm = b[4 + 2 * G + hh];
+      const float a = d * (float)(sm & 15);    // exact
+      const float bm = dmin * (float)(sm >> 4);
+#pragma unroll
+      for (int p = 0; p < 16; p++) {
+        const int e = 16 * hh + p;
+        const int q = (qs[e & 7] >> (2 * (e >> 3))) & 3;
+        const float t = a * (float)q;          // exact
+        w[e] = t - bm;                         // one rounding
+      }
+    }
+  } else if constexpr (T == GQ_Q3_K) {
+    const int G = s & 7;
+    const float d = h2f(ld2u(b));
+    const uint8_t* ql = b + 14 + 8 * G;
+    const uint32_t qh = ld4u(b + 78 + 4 * G);  // bit e: bit 2 of element 32G + e
+    const int bit = 12 * G;                    // scale fields 2G, 2G+1 of the stream
+    const uint32_t f = (ld4u(b + 2 + (bit >> 3)) >> (bit & 7)) & 0xFFFu;
+#pragma unroll
+    for (int e = 0; e < 32; e++) {
+      const int q = ((ql[e & 7] >> (2 * (e >> 3))) & 3) | (int)(((qh >> e) & 1u) << 2);
+      const int sc = (e < 16) ? (int)(f & 63u) : (int)(f >> 6);
+      w[e] = d * (float)(sc * (q - 4));        // integer first, then exact
+    }
   } else {  // GQ_Q6_K
     const int g = s & 7;
     float d = h2f(ld2u(b));
@@ -251,6 +281,85 @@ __device__ void quant_block(const float* __restrict__ w, uint8_t* out) {
         }
       }
     }
+  } else if constexpr (T == GQ_Q2_K) {
+    double hi[16], M[16], Mp[16], sp[16];
+    double maxM = 0.0, maxs = 0.0;
+    for (int i = 0; i < 16; i++) {
+      double lo = 0.0, h = -INFINITY;
+      for (int j = 0; j < 16; j++) {
+        double v = (double)w[16 * i + j];
+        lo = fmin(lo, v);
+        h = fmax(h, v);
+      }
+      hi[i] = h;
+      M[i] = -lo;
+      maxM = fmax(maxM, M[i]);
+    }
+    const uint32_t dmin16 = d_cover(maxM, 15.0);
+    const double dmin = d_h2d(dmin16);
+    int mn[16], sc[16];
+    for (int i = 0; i < 16; i++) {
+      mn[i] = (dmin == 0.0) ? 0 : d_clampi(ceil(M[i] / dmin), 0, 15);
+      Mp[i] = dmin * (double)mn[i];
+      sp[i] = (hi[i] + Mp[i]) / 3.0;
+      maxs = fmax(maxs, sp[i]);
+    }
+    const uint32_t d16 = d_cover(maxs, 15.0);
+    const double d = d_h2d(d16);
+    out[0] = (uint8_t)d16;
+    out[1] = (uint8_t)(d16 >> 8);
+    out[2] = (uint8_t)dmin16;
+    out[3] = (uint8_t)(dmin16 >> 8);
+    uint8_t q[256];
+    for (int i = 0; i < 16; i++) {
+      sc[i] = (d == 0.0) ? 0 : d_clampi(ceil(sp[i] / d), 0, 15);
+      out[4 + i] = (uint8_t)(sc[i] | (mn[i] << 4));
+      const double step = d * (double)sc[i];
+      for (int j = 0; j < 16; j++)
+        q[16 * i + j] = (uint8_t)((step == 0.0) ? 0
+                                  : d_clampi(round(((double)w[16 * i + j] + Mp[i]) / step), 0, 3));
+    }
+    for (int g = 0; g < 8; g++)                // byte 8g+k: elements 32g+k+8u at bits 2u
+      for (int k = 0; k < 8; k++)
+        out[20 + 8 * g + k] = (uint8_t)(q[32 * g + k] | (q[32 * g + k + 8] << 2) |
+                                        (q[32 * g + k + 16] << 4) | (q[32 * g + k + 24] << 6));
+  } else if constexpr (T == GQ_Q3_K) {
+    double t[16], maxt = 0.0;
+    for (int i = 0; i < 16; i++) {
+      double a = 0.0;
+      for (int j = 0; j < 16; j++) a = fmax(a, fabs((double)w[16 * i + j]));
+      t[i] = a / 3.0;
+      maxt = fmax(maxt, t[i]);
+    }
+    const uint32_t d16 = d_cover(maxt, 63.0);
+    const double d = d_h2d(d16);
+    out[0] = (uint8_t)d16;
+    out[1] = (uint8_t)(d16 >> 8);
+    uint8_t q[256];
+    uint64_t lo64 = 0, hi32 = 0;               // 16 six-bit fields, LSB-first
+    for (int i = 0; i < 16; i++) {
+      const int sc = (d == 0.0) ? 0 : d_clampi(ceil(t[i] / d), 0, 63);
+      const int sh = 6 * i;
+      if (sh + 6 <= 64) lo64 |= (uint64_t)sc << sh;
+      else if (sh >= 64) hi32 |= (uint64_t)sc << (sh - 64);
+      else { lo64 |= (uint64_t)sc << sh; hi32 |= (uint64_t)sc >> (64 - sh); }
+      const double step = d * (double)sc;
+      for (int j = 0; j < 16; j++)
+        q[16 * i + j] = (uint8_t)((step == 0.0) ? 4
+                                  : d_clampi(round((double)w[16 * i + j] / step), -3, 3) + 4);
+    }
+    for (int k = 0; k < 8; k++) out[2 + k] = (uint8_t)(lo64 >> (8 * k));
+    for (int k = 0; k < 4; k++) out[10 + k] = (uint8_t)(hi32 >> (8 * k));
+    for (int g = 0; g < 8; g++)
+      for (int k = 0; k < 8; k++)
+        out[14 + 8 * g + k] = (uint8_t)((q[32 * g + k] & 3) | ((q[32 * g + k + 8] & 3) << 2) |
+                                        ((q[32 * g + k + 16] & 3) << 4) |
+                                        ((q[32 * g + k + 24] & 3) << 6));
+    for (int k = 0; k < 32; k++) {
+      int v = 0;
+      for (int b = 0; b < 8; b++) v |= ((q[8 * k + b] >> 2) & 1) << b;
+      out[78 + k] = (uint8_t)v;
+    }
   } else {  // GQ_Q6_K
     double t[16], maxt = 0.0;
     for (int s = 0; s < 16; s++) {
@@ -327,6 +436,8 @@ hipError_t launch_dequant(int type, const void* blob, int64_t rows, int64_t cols
     case GQ_Q6_K: return dequant_t<GQ_Q6_K>(blob, rows, cols, out, f16, st);
     case GQ_Q4_1: return dequant_t<GQ_Q4_1>(blob, rows, cols, out, f16, st);
     case GQ_Q5_K: return dequant_t<GQ_Q5_K>(blob, rows, cols, out, f16, st);
+    case GQ_Q2_K: return dequant_t<GQ_Q2_K>(blob, rows, cols, out, f16, st);
+    case GQ_Q3_K: return dequant_t<GQ_Q3_K>(blob, rows, cols, out, f16, st);
   }
   return hipErrorInvalidValue;
 }
@@ -350,6 +461,8 @@ hipError_t launch_quantize(int type, const float* w, int64_t rows, int64_t cols,
     case GQ_Q6_K: return quantize_t<GQ_Q6_K>(w, rows, cols, blob, st);
     case GQ_Q4_1: return quantize_t<GQ_Q4_1>(w, rows, cols, blob, st);
     case GQ_Q5_K: return quantize_t<GQ_Q5_K>(w, rows, cols, blob, st);
+    case GQ_Q2_K: return quantize_t<GQ_Q2_K>(w, rows, cols, blob, st);
+    case GQ_Q3_K: return quantize_t<GQ_Q3_K>(w, rows, cols, blob, st);
   }
   return hipErrorInvalidValue;
 }

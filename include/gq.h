@@ -51,7 +51,9 @@ enum {
     GQ_Q4_K = 5,   /* 256 weights, 144 B: fp16 d, fp16 dmin, 12 B 6-bit sc/m, 128 B codes */
     GQ_Q6_K = 6,   /* 256 weights, 210 B: fp16 d, 16 int8 scales, 128 B low, 64 B high bits */
     GQ_Q4_1 = 7,   /* 32 weights, 20 B:  fp16 d, fp16 m, 16 B codes; w = d*q + m */
-    GQ_Q5_K = 8    /* 256 weights, 176 B: Q4_K's fields, 32 B fifth bits, 128 B codes */
+    GQ_Q5_K = 8,   /* 256 weights, 176 B: Q4_K's fields, 32 B fifth bits, 128 B codes */
+    GQ_Q2_K = 9,   /* 256 weights, 84 B: fp16 d, fp16 dmin, 16 B 4-bit sc/m, 64 B 2-bit codes */
+    GQ_Q3_K = 10   /* 256 weights, 110 B: fp16 d, 12 B 6-bit sc, 64 B low 2 bits, 32 B third bits */
 };
 
 /* Error codes. */
@@ -88,6 +90,14 @@ enum {
  *        little-endian field = bit 4 of element e's code; qs[128] @48 as in
  *        Q4_K (R: 5.5 bpw, "Other k-quants at a glance").  q in 0..31,
  *        w = (d*sc_i)*q - dmin*m_i.
+ *  Q2_K: d @0; dmin @2; 16 bytes @4, byte s = scale (low nibble) and min
+ *        (high nibble) of the 16 weights 16s..16s+15; qs[64] @20, byte 8g+k
+ *        holds the 2-bit codes of elements 32g+k+8u at bits 2u..2u+1 (R: 2.625
+ *        bpw, "Other k-quants at a glance").  w = (d*sc_s)*q - dmin*m_s.
+ *  Q3_K: d @0; 16 six-bit scales @2 in Q4_K's 96-bit stream (field s for
+ *        weights 16s..16s+15); low 2 bits of the codes @14 in Q2_K's order;
+ *        32 bytes @78, bit e = bit 2 of element e's code (R: 3.4375 bpw, same
+ *        table).  w = d*(sc_s*(q-4)), q in 0..7.
  *
  * Limits: rows, cols and n_tok below 2^31; rows*RB, n_tok*cols and
  * n_tok*rows below 2^47; cols <= 16384 at n_tok = 1 (x is staged in 64 KB of
@@ -196,11 +206,11 @@ int gq_matmul_decode(const void *weight_blob, const void *up_blob, int ggml_type
 
 /*
  * Dequantize the whole blob into out[rows][cols] (device, 16-B aligned).
- *   out_type GQ_F32: bit-exact with the stated fp32 operation order: Q4_K
- *     and Q5_K form a = d*sc and b = dmin*m in fp32 (exact) and round once
- *     in a*q - b; Q6_K forms the integer sc*(q-32) and multiplies by d
- *     (exact); Q4_1 rounds once in d*q + m (d*q exact); the other 32-weight
- *     types compute d*(q - offset) (exact).
+ *   out_type GQ_F32: bit-exact with the stated fp32 operation order: Q4_K,
+ *     Q5_K and Q2_K form a = d*sc and b = dmin*m in fp32 (exact) and round
+ *     once in a*q - b; Q6_K and Q3_K form the integer sc*(q-32) or
+ *     sc*(q-4) and multiply by d (exact); Q4_1 rounds once in d*q + m (d*q
+ *     exact); the other 32-weight types compute d*(q - offset) (exact).
  *   out_type GQ_F16: round-to-nearest-even of that fp32 value.
  */
 int gq_dequant(const void *weight_blob, int ggml_type, int64_t rows, int64_t cols,
@@ -211,8 +221,9 @@ int gq_dequant(const void *weight_blob, int ggml_type, int64_t rows, int64_t col
  * all arithmetic in fp64: symmetric absmax blocks for Q4_0 / Q5_0 / Q8_0 and
  * for Q6_K's 16-weight sub-blocks, min/scale sub-blocks for Q4_K ("two-level
  * scaling" and "asymmetric quantization", Hitchhiker's Guide §11.2; Q5_K
- * the same with 31 levels, Q4_1 a min rounded down to fp16 and a covering
- * scale per block); stored
+ * the same with 31 levels, Q2_K over 16-weight sub-blocks with 3 levels and
+ * 4-bit fields, Q3_K as Q6_K with codes -3..3 and 6-bit scales, Q4_1 a min
+ * rounded down to fp16 and a covering scale per block); stored
  * fp16 scales are rounded up so every weight is covered, codes are rounded
  * half away from zero.  Weights whose block scale would exceed the largest
  * finite fp16 saturate.  Used to make blobs from fp32 weights on the device.

@@ -76,7 +76,7 @@ def test_llama3_8b_layer(name, t, rows, cols):
         run_case(t, rows, cols, n, "f32" if n == 1 else "f16", seed=5000 + rows + cols)
 
 
-@pytest.mark.parametrize("t", ["q4_1", "q5_k"])
+@pytest.mark.parametrize("t", ["q4_1", "q5_k", "q2_k", "q3_k"])
 def test_new_types_4096(t):
     """The block types beyond the Q4_K_M recipe at a full 4096 x 4096 size,
     through the GEMV (fp32 x) and the batched paths (fp16 x)."""

@@ -28,7 +28,8 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256}
+QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256,
+      "q2_k": 256, "q3_k": 256}
 
 
 def say(msg):
@@ -62,7 +63,7 @@ PATHS = [
 ]
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_1"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q5_k", "q4_1", "q2_k", "q3_k"])
 @pytest.mark.parametrize("name,path,n", PATHS)
 @pytest.mark.parametrize("xdt", ["f32", "f16"])
 def test_row_permutation_permutes_y(t, name, path, n, xdt):
@@ -104,7 +105,7 @@ def test_linear_in_x(t, name, path, n, xdt):
     assert bool((err <= tol).all()), f"{t} {name}: linearity beyond the bound ({ratio:.3e})"
 
 
-@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q4_1", "q5_k"])
+@pytest.mark.parametrize("t", ["q4_k", "q6_k", "q8_0", "q4_1", "q5_k", "q2_k", "q3_k"])
 @pytest.mark.parametrize("n,path", [(8, None), (40, None), (70, None),
                                     (24, gq.PATH_TILED), (33, gq.PATH_WEIGHT_STREAM)])
 @pytest.mark.parametrize("xdt", ["f32", "f16"])

@@ -20,7 +20,8 @@ import synth
 
 pytestmark = pytest.mark.gpu
 
-QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256}
+QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256,
+      "q2_k": 256, "q3_k": 256}
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 TOL = 1e-3
 
@@ -113,6 +114,8 @@ GEMV_SHAPES = {
     "q4_k": [(1, 256), (37, 2304), (257, 4096), (130, 16384)],
     "q6_k": [(1, 256), (37, 2304), (257, 11008), (64, 14336)],
     "q5_k": [(1, 256), (37, 2304), (257, 4096), (130, 11008)],
+    "q2_k": [(1, 256), (37, 2304), (257, 4096), (130, 11008)],
+    "q3_k": [(1, 256), (37, 2304), (257, 4096), (64, 14336)],
     "q4_1": [(1, 32), (37, 96), (257, 4096), (33, 2080)],
     "q8_0": [(1, 32), (37, 96), (257, 4096), (33, 2080)],
     "q5_0": [(1, 32), (37, 96), (257, 4096), (33, 2080)],
@@ -134,7 +137,8 @@ def test_gemv_parity(t, xdt):
 # ---------------------------------------------------------------- matrix cores (n >= 2)
 
 MM_SHAPES = {"q4_k": (75, 512), "q6_k": (75, 768), "q8_0": (75, 352), "q5_0": (75, 288),
-             "q4_0": (75, 320), "q4_1": (75, 352), "q5_k": (75, 768)}
+             "q4_0": (75, 320), "q4_1": (75, 352), "q5_k": (75, 768), "q2_k": (75, 768),
+             "q3_k": (75, 768)}
 
 
 @pytest.mark.parametrize("t", gq.QUANT_TYPES)
@@ -343,7 +347,8 @@ def decode_reference(blob, up, t, rows, cols, x, xdt, nw, eps):
 
 DECODE_SHAPES = [("q4_k", 300, 4096), ("q6_k", 96, 11008), ("q8_0", 300, 352),
                  ("q5_0", 75, 288), ("q4_0", 130, 2048), ("q4_k", 200, 768),
-                 ("q4_1", 130, 2080), ("q5_k", 120, 4096)]
+                 ("q4_1", 130, 2080), ("q5_k", 120, 4096), ("q2_k", 120, 4096),
+                 ("q3_k", 96, 11008)]
 
 
 @pytest.mark.parametrize("t,rows,cols", DECODE_SHAPES)
@@ -437,7 +442,7 @@ def test_identity_reduction(n, xdt):
 def _scale_by_two(blob, t, rows, cols):
     qk, bb = oracle.block_info(t)
     b = blob.copy().reshape(-1, bb)
-    offs = [0, 2] if t in ("q4_k", "q5_k", "q4_1") else [0]     # d, and dmin or m
+    offs = [0, 2] if t in ("q4_k", "q5_k", "q4_1", "q2_k") else [0]     # d, and dmin or m
     for off in offs:
         h = b[:, off].astype(np.uint16) | (b[:, off + 1].astype(np.uint16) << 8)
         mag = h & 0x7FFF

@@ -17,8 +17,9 @@ from test_gpu_parity import check_matmul, say
 
 pytestmark = pytest.mark.gpu
 
-TYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k"]
-QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256}
+TYPES = ["q4_0", "q5_0", "q8_0", "q4_k", "q6_k", "q4_1", "q5_k", "q2_k", "q3_k"]
+QK = {"q4_0": 32, "q5_0": 32, "q8_0": 32, "q4_k": 256, "q6_k": 256, "q4_1": 32, "q5_k": 256,
+      "q2_k": 256, "q3_k": 256}
 PATHS = {"auto": gq.PATH_AUTO, "stream": gq.PATH_WEIGHT_STREAM, "tiled": gq.PATH_TILED}
 
 

@@ -32,7 +32,8 @@ pytestmark = pytest.mark.gpu
 QK = tol_terms.QK
 THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 SHAPES = {"q4_k": (75, 768), "q6_k": (70, 768), "q8_0": (75, 352), "q5_0": (75, 288),
-          "q4_0": (75, 320), "q4_1": (75, 352), "q5_k": (70, 768)}
+          "q4_0": (75, 320), "q4_1": (75, 352), "q5_k": (70, 768), "q2_k": (70, 768),
+          "q3_k": (70, 768)}
 BATCH_PATHS = [("auto", gq.PATH_AUTO), ("stream", gq.PATH_WEIGHT_STREAM),
                ("tiled", gq.PATH_TILED)]
 
