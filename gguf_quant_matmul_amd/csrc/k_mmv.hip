@@ -737,6 +737,9 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #ifndef GQ_MMV_WAVES
 #define GQ_MMV_WAVES 4096                     // target waves per launch
 #endif
+#ifndef GQ_MMV_WAVES8
+#define GQ_MMV_WAVES8 2048                    // the same for 8-token passes of fp16 x
+#endif
 #ifndef GQ_MMV_DEPTH32                        // ring depth of the 32-token passes
 #define GQ_MMV_DEPTH32 1
 #endif
@@ -750,10 +753,10 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #define GQ_MMV_RT2_TILES 2000
 #endif
 
-// KS: enough waves to cover the chip GQ_MMV_WAVES / 256 deep, at most 8 per
+// KS: enough waves to cover the chip waves / 256 deep (waves: the launch's target), at most 8 per
 // workgroup (and as many as the LDS budget holds), and no more than the row has
 // slabs.
-int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt) {
+int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt, int waves) {
   const int64_t tiles = (rows + 16 * rt - 1) / (16 * rt), passes = (n + p - 1) / p;
   const int64_t nslab = (cols + 255) / 256;
   int ks = 1;
@@ -761,7 +764,7 @@ int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int 
   // top of 16 KB of activations per wave) may take 96 KB, so 4 waves still
   // split a long row (Q8_0 4096 x 11008 at 32 tokens: 39.6 -> 28.8 us)
   const int budget = (p == 32 && tiles * passes <= 256) ? 98304 : 65536;
-  while (ks < 8 && (ks * 2) * lds_per_wave <= budget && tiles * passes * ks * 2 <= GQ_MMV_WAVES &&
+  while (ks < 8 && (ks * 2) * lds_per_wave <= budget && tiles * passes * ks * 2 <= waves &&
          ks * 2 <= nslab)
     ks *= 2;
   return ks;
@@ -774,15 +777,21 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   constexpr int D = XLO ? (P == 8 ? 2 : 1) : (P == 32) ? GQ_MMV_DEPTH32
                    : (T == GQ_Q5_0 && P == 16) ? 2 : GQ_MMV_DEPTH;
   constexpr int XB = P * 512 * (XLO ? 2 : 1) + kWB<T> + kSB<XLO>;
+  // 8-token passes of fp16 x: half the waves, each splitting its row's slabs
+  // over fewer waves, so a workgroup reads the activation block once for
+  // twice the work (measured on MI355X: Q4_K 11008x4096 at 8 tokens 12.2 ->
+  // 11.6 us, 14336x4096 14.7 -> 13.6 us, 22016x4096 20.5 -> 19.3 us; Q6_K
+  // and fp32 x gain nothing or lose)
+  constexpr int WAVES = (P == 8 && !XLO) ? GQ_MMV_WAVES8 : GQ_MMV_WAVES;
   // Tall K-quant matrices: two 16-row tiles per wave share each activation
   // slab, halving the activation reads, which there outweigh the weights'
   // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;
   // with fewer tiles the halved wave count costs more than it saves)
   if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K || T == GQ_Q2_K || T == GQ_Q3_K) {
     if ((rows + 15) / 16 >= GQ_MMV_RT2_TILES)
-      return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2), st);
+      return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2, WAVES), st);
   }
-  return mmv_launch<T, XLO, P, D, 1>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 1), st);
+  return mmv_launch<T, XLO, P, D, 1>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 1, WAVES), st);
 }
 
 template <int T, bool XLO>
