@@ -783,12 +783,17 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // 11.6 us, 14336x4096 14.7 -> 13.6 us, 22016x4096 20.5 -> 19.3 us; Q6_K
   // and fp32 x gain nothing or lose)
   constexpr int WAVES = (P == 8 && !XLO) ? GQ_MMV_WAVES8 : GQ_MMV_WAVES;
-  // Tall K-quant matrices: two 16-row tiles per wave share each activation
-  // slab, halving the activation reads, which there outweigh the weights'
-  // (measured: Q6_K 128256 x 4096 at 24 / 32 tokens 201 / 216 -> 164 / 171 us;
-  // with fewer tiles the halved wave count costs more than it saves)
+  // Two 16-row tiles per wave share each activation slab, halving the
+  // activation reads, which outweigh the weights' on tall matrices and in
+  // 32-token passes; they pay once the halved tile count still gives 256
+  // workgroups (measured on MI355X: Q6_K 128256 x 4096 at 24 / 32 tokens
+  // 201 / 216 -> 164 / 171 us; 32-token passes of Q4_K 11008 x 4096 at 24 /
+  // 32 / 64 tokens 21.5 / 22.4 / 35.0 -> 18.6 / 20.3 / 27.9 us, Q6_K
+  // 4096 x 11008 at 64 tokens 42.5 -> 38.8 us; with fewer workgroups, 4096
+  // rows at 32 tokens, 10.8 -> 14.4 us)
   if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K || T == GQ_Q2_K || T == GQ_Q3_K) {
-    if ((rows + 15) / 16 >= GQ_MMV_RT2_TILES)
+    const int64_t tiles = (rows + 15) / 16, passes = (n + P - 1) / P;
+    if (tiles >= GQ_MMV_RT2_TILES || (P == 32 && tiles / 2 * passes >= 256))
       return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2, WAVES), st);
   }
   return mmv_launch<T, XLO, P, D, 1>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 1, WAVES), st);
@@ -800,11 +805,11 @@ hipError_t mmv_t(const void* blob, int64_t rows, int64_t cols, const void* x, in
   if (n <= 8) return mmv_p<T, XLO, 8>(blob, rows, cols, x, n, y, st);
   // 32-token passes (fp16 x) halve the decode work per token, which is what
   // bounds the 32-weight types and Q6_K; they need at least 256 workgroups
-  // (16-row tiles x passes) to cover the chip, and for Q4_K, whose decode is
-  // cheap, they only pay up to 512 row tiles (measured on MI355X).
+  // (16-row tiles x passes) to cover the chip.  Q4_K's decode is cheap, and
+  // past 512 row tiles its 32-token passes pay only because they then take
+  // two row tiles per wave (mmv_p).
   const int64_t tiles = (rows + 15) / 16, passes32 = (n + 31) / 32;
-  const bool p32 = !XLO && n > GQ_MMV_P32_FROM && tiles * passes32 >= 256 &&
-                   (T != GQ_Q4_K || tiles <= 512);
+  const bool p32 = !XLO && n > GQ_MMV_P32_FROM && tiles * passes32 >= 256;
   if (!p32) return mmv_p<T, XLO, 16>(blob, rows, cols, x, n, y, st);
   return mmv_p<T, false, 32>(blob, rows, cols, x, n, y, st);
 }

@@ -197,10 +197,15 @@ def test_mmv_32weight_staged(t, rows, cols, n, xdt):
 @pytest.mark.parametrize("t,rows,cols,ns", [
     ("q4_k", 32768, 256, ((5, "f16"), (24, "f16"), (8, "f32"))),
     ("q6_k", 32005, 512, ((8, "f16"), (30, "f16"), (3, "f32"))),
+    ("q4_k", 11008, 512, ((24, "f16"), (64, "f16"))),   # 32-token passes, 344 tile pairs
+    ("q5_k", 4112, 512, ((40, "f16"),)),                 # 257 tiles: the last pair has one
+    ("q3_k", 8208, 256, ((20, "f16"),)),
+    ("q2_k", 8200, 256, ((33, "f16"),)),                 # 513 tiles, the last one ragged
 ])
 def test_mmv_two_tiles_per_wave(t, rows, cols, ns):
-    """Tall K-quant matrices (over 2000 16-row tiles), where each wave takes
-    two tiles sharing its activation slab; the last tile ragged: sampled rows
+    """Tall K-quant matrices (over 2000 16-row tiles), and 32-token passes
+    whose tile pairs still make 256 workgroups, where each wave takes two
+    tiles sharing its activation slab; the last tile ragged: sampled rows
     (every token) against the oracle."""
     _, blob = quantized(t, rows, cols, seed=141)
     bd = to_dev(blob)
