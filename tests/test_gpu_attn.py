@@ -75,7 +75,9 @@ SHAPES = [("q8_0", 1, 2, 4, 128, 1.0),       # one position: the value row
           ("q8_0", 700, 4, 4, 128, 1.0),     # one query head per KV head
           ("q4_0", 2048, 8, 16, 128, 2.0),   # whole chunks only, 2 heads per KV head
           ("q8_0", 513, 2, 32, 256, 1.0),    # head_dim 256, 16 heads per KV head
-          ("q8_0", 8192, 1, 8, 128, 1.0)]    # one KV head, 8 query heads, 128 whole chunks
+          ("q8_0", 8192, 1, 8, 128, 1.0),    # one KV head, 8 query heads, 128 whole chunks
+          ("q8_0", 32868, 8, 40, 128, 1.0),  # 129 chunks per KV head, the last ragged
+          ("q4_0", 16400, 16, 32, 128, 2.0)]  # 65 chunks x 16 KV heads
 
 
 @pytest.mark.parametrize("t,kv_len,n_kv,n_heads,head_dim,qs", SHAPES)
