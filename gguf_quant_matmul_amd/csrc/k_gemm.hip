@@ -91,6 +91,13 @@ template <> struct BR<GQ_Q4_K> {
     if constexpr (HDR) hd = bld16(R, vo, 0);
     q = bld16(R, vo + 16 * (sg & 7), 16);
   }
+  // fields at FL * fk + FU * (step % 4) + FB of the super-block (see SbFields)
+  static constexpr int NF = 2, FL[NF] = {0, 16}, FU[NF] = {0, 32}, FB[NF] = {0, 16};
+  template <bool HDR = true>
+  __device__ void load_at(__amdgpu_buffer_rsrc_t R, const uint32_t (&o)[NF]) {
+    if constexpr (HDR) hd = bld16(R, (int)o[0], 0);
+    q = bld16(R, (int)o[1], 0);
+  }
   // largest |w| the block's fields allow: 945 |d| + 63 |dmin|
   __device__ static float bound(const u32x4& hd) {
     return fmaf(945.f, fabsf(h2f(hd.x)), 63.f * fabsf(h2f(hd.x >> 16)));
@@ -129,6 +136,13 @@ template <> struct BR<GQ_Q5_K> {
     if constexpr (HDR) hd = bld16(R, vo, 0);
     qh = bld4(R, vo + 4 * (sg & 7), 16);
     q = bld16(R, vo + 16 * (sg & 7), 48);
+  }
+  static constexpr int NF = 3, FL[NF] = {0, 4, 16}, FU[NF] = {0, 8, 32}, FB[NF] = {0, 16, 48};
+  template <bool HDR = true>
+  __device__ void load_at(__amdgpu_buffer_rsrc_t R, const uint32_t (&o)[NF]) {
+    if constexpr (HDR) hd = bld16(R, (int)o[0], 0);
+    qh = bld4(R, (int)o[1], 0);
+    q = bld16(R, (int)o[2], 0);
   }
   __device__ static float bound(const u32x4& hd) {          // 63 * 31 |d| + 63 |dmin|
     return fmaf(1953.f, fabsf(h2f(hd.x)), 63.f * fabsf(h2f(hd.x >> 16)));
@@ -199,6 +213,15 @@ template <> struct BR<GQ_Q6_K> {
     sc = bld2(R, vo + 2 * G, 2);
     d = bld2(R, vo, 0);
   }
+  static constexpr int NF = 4, FL[NF] = {16, 8, 2, 0}, FU[NF] = {32, 16, 4, 0},
+                       FB[NF] = {18, 146, 2, 0};
+  template <bool HDR = true>
+  __device__ void load_at(__amdgpu_buffer_rsrc_t R, const uint32_t (&o)[NF]) {
+    ql = bld16(R, (int)o[0], 0);
+    qh = bld8(R, (int)o[1], 0);
+    sc = bld2(R, (int)o[2], 0);
+    d = bld2(R, (int)o[3], 0);
+  }
   __device__ float bound() const { return 4096.f * fabsf(h2f(d)); }   // |sc (q - 32)| <= 4096
   __device__ void decode(int, int k, u32x4 out[4]) const {
     const float dd = __builtin_ldexpf(h2f(d), k);
@@ -238,6 +261,13 @@ template <> struct BR<GQ_Q2_K> {
     sm = bld2(R, vo + 2 * G, 4);
     q = bld8(R, vo + 8 * G, 20);
   }
+  static constexpr int NF = 3, FL[NF] = {0, 2, 8}, FU[NF] = {0, 4, 16}, FB[NF] = {0, 4, 20};
+  template <bool HDR = true>
+  __device__ void load_at(__amdgpu_buffer_rsrc_t R, const uint32_t (&o)[NF]) {
+    dm = bld4(R, (int)o[0], 0);
+    sm = bld2(R, (int)o[1], 0);
+    q = bld8(R, (int)o[2], 0);
+  }
   // largest |w| the fields allow: 15 * 3 |d| + 15 |dmin|
   __device__ float bound() const { return fmaf(45.f, fabsf(h2f(dm)), 15.f * fabsf(h2f(dm >> 16))); }
   __device__ void decode(int, int k, u32x4 out[4]) const {
@@ -270,6 +300,15 @@ template <> struct BR<GQ_Q3_K> {
     sc = bld4(R, vo + ((12 * G) >> 3), 2);
     q = bld8(R, vo + 8 * G, 14);
     qh = bld4(R, vo + 4 * G, 78);
+  }
+  // sc: (12 G) >> 3 = 3 (step % 4) + fk for G = 2 (step % 4) + fk
+  static constexpr int NF = 4, FL[NF] = {0, 1, 8, 4}, FU[NF] = {0, 3, 16, 8}, FB[NF] = {0, 2, 14, 78};
+  template <bool HDR = true>
+  __device__ void load_at(__amdgpu_buffer_rsrc_t R, const uint32_t (&o)[NF]) {
+    d = bld2(R, (int)o[0], 0);
+    sc = bld4(R, (int)o[1], 0);
+    q = bld8(R, (int)o[2], 0);
+    qh = bld4(R, (int)o[3], 0);
   }
   __device__ float bound() const { return 252.f * fabsf(h2f(d)); }   // |sc (q - 4)| <= 252
   __device__ void decode(int sg, int k, u32x4 out[4]) const {
@@ -359,6 +398,22 @@ template <bool XLO, int NT, int BM> struct AR {
   u32x4 v[N];
 };
 
+// A super-block type's field offsets for the tiled kernel's loads: field f of
+// the segment 2 * step + fk sits at FL[f] * fk + FU[f] * (step % 4) + FB[f]
+// bytes into super-block step / 4 (the 32-weight types have none: N = 1).
+template <int T, bool = (Geo<T>::QK == 256)> struct SbFields {
+  static constexpr int N = 1;
+  __device__ static constexpr int fl(int) { return 0; }
+  __device__ static constexpr int fu(int) { return 0; }
+  __device__ static constexpr int fb(int) { return 0; }
+};
+template <int T> struct SbFields<T, true> {
+  static constexpr int N = BR<T>::NF;
+  __device__ static constexpr int fl(int f) { return BR<T>::FL[f]; }
+  __device__ static constexpr int fu(int f) { return BR<T>::FU[f]; }
+  __device__ static constexpr int fb(int f) { return BR<T>::FB[f]; }
+};
+
 }  // namespace
 
 // VALU instructions placed after each MFMA (measured best: 5; Q6_K 2, whose
@@ -399,7 +454,7 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
   if (q >= total) return;                    // whole workgroup: uniform
   const int n0 = (q / tm) * BN, m0 = (q % tm) * BM;
 
-  const int kg = (KS > 1) ? (int)threadIdx.x / NT : 0;   // K group
+  const int kg = (KS > 1) ? uniform((int)threadIdx.x / NT) : 0;   // K group
   const int tid = (int)threadIdx.x - kg * NT, lane = tid & 63, w = tid >> 6;
   uint8_t* const Ag = As + kg * 2 * NA * ATILE;          // the group's activation tiles
   int* const dtok = xk + kg * XKG;           // [2][BM]
@@ -440,15 +495,39 @@ __global__ void __launch_bounds__(2 * BN * KS) k_gemm(const uint8_t* __restrict_
   constexpr bool SHARE = BR<T>::kHeader && D == 4;
   // s: the group's step (global step kbase + s); steps past the group's
   // range (or the row) read zeros
+  // Super-block types (every row a whole number of K steps): each load's
+  // offset is a per-lane part fixed for the launch plus a part common to the
+  // wave for the step (kOobOff for steps past the group's range, which puts
+  // the sum past every resource: the load reads zero), so a step's address
+  // arithmetic is one vector add per load.
+  constexpr bool SB = Geo<T>::QK == 256;
+  uint32_t lf[SbFields<T>::N];               // per-lane field offsets
+  if constexpr (SB) {
+#pragma unroll
+    for (int f = 0; f < SbFields<T>::N; f++)
+      lf[f] = (uint32_t)(vrow + SbFields<T>::fl(f) * fk + SbFields<T>::fb(f));
+  }
   auto load = [&](AR<XLO, NT, BM>& a, BR<T>& b, int s, auto hdr) __attribute__((always_inline)) {
     const int gs = kbase + s;
     const bool in = gs < kend;
-    const int sg = 2 * gs + fk;
-    b.template load<decltype(hdr)::value>(WR, vrow, sg, in && sg < nseg);
-    const int col = gs * BK + xc;
+    if constexpr (SB) {
+      uint32_t o[SbFields<T>::N];
 #pragma unroll
-    for (int i = 0; i < NL; i++)
-      a.v[i] = bld16(XR, (in && col < cols) ? xo[i] + gs * BK * ES : kOobOff, 0);
+      for (int f = 0; f < SbFields<T>::N; f++)
+        o[f] = lf[f] + (in ? (uint32_t)((gs >> 2) * Geo<T>::BB + SbFields<T>::fu(f) * (gs & 3))
+                           : (uint32_t)kOobOff);
+      b.template load_at<decltype(hdr)::value>(WR, o);
+      const uint32_t ux = in ? (uint32_t)(gs * BK * ES) : (uint32_t)kOobOff;
+#pragma unroll
+      for (int i = 0; i < NL; i++) a.v[i] = bld16(XR, (int)((uint32_t)xo[i] + ux), 0);
+    } else {
+      const int sg = 2 * gs + fk;
+      b.template load<decltype(hdr)::value>(WR, vrow, sg, in && sg < nseg);
+      const int col = gs * BK + xc;
+#pragma unroll
+      for (int i = 0; i < NL; i++)
+        a.v[i] = bld16(XR, (in && col < cols) ? xo[i] + gs * BK * ES : kOobOff, 0);
+    }
   };
   // fp32 x: thread slot i always stages the same token, 16 threads per token
   // and step; kx[i] is that token's exponent k (x enters as hi + lo of
