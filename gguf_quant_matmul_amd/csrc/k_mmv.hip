@@ -740,6 +740,9 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #ifndef GQ_MMV_WAVES8
 #define GQ_MMV_WAVES8 2048                    // the same for 8-token passes of fp16 x
 #endif
+#ifndef GQ_MMV_WAVES32
+#define GQ_MMV_WAVES32 2048                   // the same for 32-token passes
+#endif
 #ifndef GQ_MMV_DEPTH32                        // ring depth of the 32-token passes
 #define GQ_MMV_DEPTH32 1
 #endif
@@ -782,7 +785,10 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // twice the work (measured on MI355X: Q4_K 11008x4096 at 8 tokens 12.2 ->
   // 11.6 us, 14336x4096 14.7 -> 13.6 us, 22016x4096 20.5 -> 19.3 us; Q6_K
   // and fp32 x gain nothing or lose)
-  constexpr int WAVES = (P == 8 && !XLO) ? GQ_MMV_WAVES8 : GQ_MMV_WAVES;
+  // 32-token passes likewise (Q4_K 22016x4096 at 32 tokens 30.5 -> 28.3 us,
+  // 11008x4096 at 48 27.5 -> 26.2 us; the other shapes measured are capped
+  // by the LDS budget first and do not change)
+  constexpr int WAVES = (P == 8 && !XLO) ? GQ_MMV_WAVES8 : (P == 32) ? GQ_MMV_WAVES32 : GQ_MMV_WAVES;
   // Two 16-row tiles per wave share each activation slab, halving the
   // activation reads, which outweigh the weights' on tall matrices and in
   // 32-token passes; they pay once the halved tile count still gives 256
