@@ -759,7 +759,9 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 // KS: enough waves to cover the chip waves / 256 deep (waves: the launch's target), at most 8 per
 // workgroup (and as many as the LDS budget holds), and no more than the row has
 // slabs.
-int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt, int waves) {
+// KS <= kmax.
+int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt, int waves,
+            int kmax = 8) {
   const int64_t tiles = (rows + 16 * rt - 1) / (16 * rt), passes = (n + p - 1) / p;
   const int64_t nslab = (cols + 255) / 256;
   int ks = 1;
@@ -767,7 +769,7 @@ int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int 
   // top of 16 KB of activations per wave) may take 96 KB, so 4 waves still
   // split a long row (Q8_0 4096 x 11008 at 32 tokens: 39.6 -> 28.8 us)
   const int budget = (p == 32 && tiles * passes <= 256) ? 98304 : 65536;
-  while (ks < 8 && (ks * 2) * lds_per_wave <= budget && tiles * passes * ks * 2 <= waves &&
+  while (ks < kmax && (ks * 2) * lds_per_wave <= budget && tiles * passes * ks * 2 <= waves &&
          ks * 2 <= nslab)
     ks *= 2;
   return ks;
@@ -797,12 +799,20 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // 32 / 64 tokens 21.5 / 22.4 / 35.0 -> 18.6 / 20.3 / 27.9 us, Q6_K
   // 4096 x 11008 at 64 tokens 42.5 -> 38.8 us; with fewer workgroups, 4096
   // rows at 32 tokens, 10.8 -> 14.4 us)
+  // 16-token passes of fp16 x: at most 4 waves per tile (with 8 each wave
+  // has two slabs, and 8192 x 4096 at 16 tokens took 14.2 us against 11.7 with
+  // 4), and two tiles per wave from 448 tile pairs (14336 x 4096: 19.2 -> 16.1
+  // us, 22016 x 4096: 24.1 -> 22.3 us; 11008 x 4096, 344 pairs, 15.2 -> 15.8)
+  constexpr int KMAX = (P == 16 && !XLO) ? 4 : 8;
   if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K || T == GQ_Q2_K || T == GQ_Q3_K) {
     const int64_t tiles = (rows + 15) / 16, passes = (n + P - 1) / P;
-    if (tiles >= GQ_MMV_RT2_TILES || (P == 32 && tiles / 2 * passes >= 256))
-      return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 2, WAVES), st);
+    if (tiles >= GQ_MMV_RT2_TILES || (P == 32 && tiles / 2 * passes >= 256) ||
+        (P == 16 && !XLO && tiles / 2 * passes >= 448))
+      return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y,
+                                         pick_ks(rows, cols, n, P, XB, 2, WAVES, KMAX), st);
   }
-  return mmv_launch<T, XLO, P, D, 1>(blob, rows, cols, x, n, y, pick_ks(rows, cols, n, P, XB, 1, WAVES), st);
+  return mmv_launch<T, XLO, P, D, 1>(blob, rows, cols, x, n, y,
+                                     pick_ks(rows, cols, n, P, XB, 1, WAVES, KMAX), st);
 }
 
 template <int T, bool XLO>
