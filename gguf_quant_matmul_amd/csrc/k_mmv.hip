@@ -802,12 +802,17 @@ hipError_t mmv_p(const void* blob, int64_t rows, int64_t cols, const void* x, in
   // 16-token passes of fp16 x: at most 4 waves per tile (with 8 each wave
   // has two slabs, and 8192 x 4096 at 16 tokens took 14.2 us against 11.7 with
   // 4), and two tiles per wave from 448 tile pairs (14336 x 4096: 19.2 -> 16.1
-  // us, 22016 x 4096: 24.1 -> 22.3 us; 11008 x 4096, 344 pairs, 15.2 -> 15.8)
+  // us, 22016 x 4096: 24.1 -> 22.3 us; 11008 x 4096, 344 pairs, 15.2 -> 15.8).
+  // fp32 x, whose 16-token slab fills the registers (a 1-deep ring): two
+  // tiles per wave from 600 tile pairs x passes (11008 x 4096 at 32 / 64
+  // tokens 56.5 / 99.4 -> 37.9 / 70.4 us, 22016 x 4096 at 16 57.4 -> 38.7,
+  // 14336 x 4096 at 32 66.1 -> 40.4; at 448 or 512, 14336 x 4096 at 16 and
+  // 8192 x 4096 at 32, they lose 12 %)
   constexpr int KMAX = (P == 16 && !XLO) ? 4 : 8;
   if constexpr (T == GQ_Q4_K || T == GQ_Q6_K || T == GQ_Q5_K || T == GQ_Q2_K || T == GQ_Q3_K) {
     const int64_t tiles = (rows + 15) / 16, passes = (n + P - 1) / P;
     if (tiles >= GQ_MMV_RT2_TILES || (P == 32 && tiles / 2 * passes >= 256) ||
-        (P == 16 && !XLO && tiles / 2 * passes >= 448))
+        (P == 16 && tiles / 2 * passes >= (XLO ? 600 : 448)))
       return mmv_launch<T, XLO, P, D, 2>(blob, rows, cols, x, n, y,
                                          pick_ks(rows, cols, n, P, XB, 2, WAVES, KMAX), st);
   }

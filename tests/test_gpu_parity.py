@@ -201,12 +201,15 @@ def test_mmv_32weight_staged(t, rows, cols, n, xdt):
     ("q5_k", 4112, 512, ((40, "f16"),)),                 # 257 tiles: the last pair has one
     ("q3_k", 8208, 256, ((20, "f16"),)),
     ("q2_k", 8200, 256, ((33, "f16"),)),                 # 513 tiles, the last one ragged
+    ("q4_k", 14352, 256, ((12, "f16"),)),                # 16-token pass, 449 pairs, ragged
+    ("q6_k", 11008, 256, ((20, "f32"),)),                # fp32 x, 344 pairs x 2 passes
+    ("q5_k", 19216, 256, ((16, "f32"),)),                # fp32 x, 601 pairs, ragged
 ])
 def test_mmv_two_tiles_per_wave(t, rows, cols, ns):
-    """Tall K-quant matrices (over 2000 16-row tiles), and 32-token passes
-    whose tile pairs still make 256 workgroups, where each wave takes two
-    tiles sharing its activation slab; the last tile ragged: sampled rows
-    (every token) against the oracle."""
+    """Tall K-quant matrices (over 2000 16-row tiles), and 16- and 32-token
+    passes with enough tile pairs, where each wave takes two tiles sharing
+    its activation slab; the last tile ragged: sampled rows (every token)
+    against the oracle."""
     _, blob = quantized(t, rows, cols, seed=141)
     bd = to_dev(blob)
     rng = np.random.default_rng(142)
