@@ -204,6 +204,7 @@ def test_mmv_32weight_staged(t, rows, cols, n, xdt):
     ("q4_k", 14352, 256, ((12, "f16"),)),                # 16-token pass, 449 pairs, ragged
     ("q6_k", 11008, 256, ((20, "f32"),)),                # fp32 x, 344 pairs x 2 passes
     ("q5_k", 19216, 256, ((16, "f32"),)),                # fp32 x, 601 pairs, ragged
+    ("q4_k", 11008, 256, ((64, "f32"),)),                # fp32 x, four passes
 ])
 def test_mmv_two_tiles_per_wave(t, rows, cols, ns):
     """Tall K-quant matrices (over 2000 16-row tiles), and 16- and 32-token
