@@ -756,10 +756,9 @@ hipError_t mmv_launch(const void* blob, int64_t rows, int64_t cols, const void* 
 #define GQ_MMV_RT2_TILES 2000
 #endif
 
-// KS: enough waves to cover the chip waves / 256 deep (waves: the launch's target), at most 8 per
-// workgroup (and as many as the LDS budget holds), and no more than the row has
-// slabs.
-// KS <= kmax.
+// KS: enough waves to cover the chip waves / 256 deep (waves: the launch's
+// target), at most kmax per workgroup (and as many as the LDS budget holds),
+// and no more than the row has slabs.
 int pick_ks(int64_t rows, int64_t cols, int64_t n, int p, int lds_per_wave, int rt, int waves,
             int kmax = 8) {
   const int64_t tiles = (rows + 16 * rt - 1) / (16 * rt), passes = (n + p - 1) / p;
