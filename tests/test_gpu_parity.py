@@ -244,6 +244,9 @@ def test_mmv_tall_matrices(t, rows, cols, ns):
     ("q6_k", 512, 4096, 200, "f32"),     # 4 tiles (2 x 2, the token tiles ragged), fp32 x
     ("q8_0", 600, 2400, 96, "f16"),      # 3 x 1 tiles, 38 K steps: a partial last unit
     ("q5_0", 300, 1056, 140, "f32"),     # 17 K steps, ragged rows and tokens
+    ("q6_k", 4096, 512, 200, "f16"),     # 64 x 64 tiles in 4 K groups, ragged token tile
+    ("q4_0", 4000, 1056, 150, "f16"),    # the same with ragged rows; 17 K steps: groups
+                                         # of 8, 8, 1 and none
 ])
 def test_gemm_few_tiles(t, rows, cols, n, xdt):
     """Prefill shapes with few tiles and long or ragged K (a partial last
