@@ -792,7 +792,9 @@ hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, i
 //     that (8192 x 4096 23.0, Q6_K 4096 x 11008 162 -> 72); no split past
 //     256 64-row tiles, where 128 x 64 tiles already fill the chip (Q4_K
 //     22016 x 4096 37.4 against 49.8 split, Q6_K 128256 x 4096 269 against 330);
-//   * 129-256 tokens: 64 x 64 tiles in 4 K groups while those fit 256 CUs;
+//   * up to 256 tokens: 64 x 64 tiles in 4 K groups while those fit 256 CUs
+//     and 128 x 64 tiles would be more than 64 (below 129 tokens, 128 or
+//     more);
 //   * more tokens: 256 x 128 tiles when they cover 128 to 256 CUs once,
 //     128 x 128 past that, 128 x 64 below (Q4_K 4096 x 4096 at 512 tokens
 //     62 -> 37); 32-row split-K tiles when even 128 x 64 tiles are fewer than
@@ -814,12 +816,16 @@ int gemm_tile_config(int type, int64_t rows, int64_t cols, int64_t n_tok, bool x
       if ((rows + 63) / 64 > 256) return 2;  // enough 128-row tiles: no split
       return (rows + 31) / 32 > 256 ? 4 : 3;
     }
-    // 129-256 tokens on few rows: 64 x 64 split tiles while they fit the
-    // chip in one round (4096 x 4096 at 192 / 256 tokens 29.1 / 30.8 ->
-    // 24.1 / 24.7 us, Q6_K 4096 x 11008 110 / 138 -> 98 / 97 us, Q6_K
-    // 4096 x 14336 at 256 172 -> 118 us; at 128 tokens 32-row tiles stay
-    // ahead, past 256 the unsplit tiles)
-    if (n_tok > 128 && n_tok <= 256 && (rows + 63) / 64 * ((n_tok + 63) / 64) <= 256) return 4;
+    // up to 256 tokens on few rows: 32-row split tiles up to 128 tokens
+    // while 128 x 64 tiles would be fewer than 128, else 64 x 64 split tiles
+    // while they fit the chip in one round and 128 x 64 tiles would be more
+    // than 64 (4096 x 4096 at 192 / 256 tokens 29.1 / 30.8 -> 24.1 / 24.7 us,
+    // 8192 x 4096 at 96 / 128 30.8 / 31.2 -> 24.5 / 25.9, Q6_K 4096 x 11008
+    // at 192 / 256 110 / 138 -> 98 / 97, Q6_K 4096 x 14336 at 256 172 -> 118;
+    // on fewer rows the 32-row tiles stay ahead: 2048 x 2048 at 160 tokens
+    // 13.3 against 19.6 us; past 256 tokens the unsplit tiles)
+    if (t128x64 < 128 && n_tok <= 128) return 3;
+    if (n_tok <= 256 && t128x64 > 64 && (rows + 63) / 64 * ((n_tok + 63) / 64) <= 256) return 4;
     if (t128x64 < 128) return 3;
     if (type == GQ_Q6_K && t128x64 <= 256) return 5;
   }
