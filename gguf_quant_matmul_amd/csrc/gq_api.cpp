@@ -63,7 +63,11 @@ bool small_batch_chunks_faster(int type, int64_t rows, int64_t cols, int64_t n_t
   const double pass_us = (double)rows * (double)cols * 32.0 / rate * 1e6 * (x_f16 ? 1.0 : 1.9);
   const int64_t k = (n_tok + 63) / 64, base = n_tok / k, extra = n_tok % k;
   const int64_t passes = extra * ((base + 16) / 16) + (k - extra) * ((base + 15) / 16);
-  const double mmv_us = (double)passes * pass_us;
+  // every chunk after the first is a launch of its own, whose start follows
+  // the previous launch's tail (~2 us measured: Q4_K 4096x4096 at 80 / 96
+  // tokens take 25.7 / 26.1 us on the weight stream against 20.8 / 21.2
+  // tiled, while Q6_K 4096x14336 at 100 tokens takes 81 against 86)
+  const double mmv_us = (double)passes * pass_us + 2.0 * (double)(k - 1);
   return mmv_us < gemm_us;
 }
 
