@@ -774,7 +774,12 @@ hipError_t gemm_t(const void* blob, int64_t rows, int64_t cols, const void* x, i
     // split K: one-wave groups stage 8 loads per step each, so their ring is
     // 2 deep (4 would cost a wave per SIMD)
     if (c == 3) return gemm_cfg<T, false, 32, 64, 4, 2>(blob, rows, cols, x, n, y, st);
-    if (c == 4) return gemm_cfg<T, false, 64, 64, 4, 4>(blob, rows, cols, x, n, y, st);
+    // 64 x 64 split tiles: a 4-deep ring where the super-block header is
+    // shared over its 4 steps (Q4_K, Q5_K), else 2 deep (measured on
+    // MI355X: Q6_K 11008x4096 at 64 tokens 40.6 -> 37.8 us, 4096x14336 at 256
+    // 118 -> 111 us, Q2_K / Q3_K / Q4_0 / Q5_0 / Q4_1 / Q8_0 -4 to -7 %;
+    // Q4_K +6 to +8 % at 2)
+    if (c == 4) return gemm_cfg<T, false, 64, 64, 4, BR<T>::kHeader ? 4 : 2>(blob, rows, cols, x, n, y, st);
     if (c == 5) return gemm_cfg<T, false, 64, 128, 2, 2>(blob, rows, cols, x, n, y, st);
   }
   if (c == 1) return gemm_cfg<T, XLO, 128, 128>(blob, rows, cols, x, n, y, st);
