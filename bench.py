@@ -273,7 +273,10 @@ def kernel_time_ms(mat, steps, per_graph=16, spread=False):
             for j in range(per_graph):
                 mat.launch(gi * per_graph + j, sp)
         graphs.append(capture(fn))
-    ms = time_graphs(graphs, max(4, steps // per_graph), warmup=2)
+    # eight warmup replays: the compute-bound shapes run a few percent slower
+    # in the first milliseconds after lighter work (the 512-token GEMM: 72.6
+    # us with two, 68.9 with eight)
+    ms = time_graphs(graphs, max(4, steps // per_graph), warmup=8)
     if spread:
         return ms / per_graph, replay_spread(graphs, 32, per_graph)
     return ms / per_graph
